@@ -1,0 +1,174 @@
+/*
+ * mla_decode.h - C ABI of the MI355X (gfx950) single-token MLA decode library.
+ *
+ * Operation (kernelindex.com "kernelbot-amd-mixed-mla-695854", the chunked
+ * torch attention fallback; "kernelbot-amd-mixed-mla-668813", the module
+ * constants): DeepSeek-style multi-head latent attention decode with one query
+ * token per request, 16 query heads sharing a single latent KV head of width
+ * 576 (512 latent + 64 rope).  For request b and head h
+ *
+ *     out[b,h,:] = bf16( softmax_t( q[b,h,:] . k_t / sqrt(576) ) @ v_t )
+ *
+ * where k_t is the dequantised 576-wide cache row of token t and v_t its first
+ * 512 entries.  The work is split over the KV sequence (split-K "flash
+ * decoding", page 668813's mxfp4 stage-1/stage-2 kernels): stage 1 produces a
+ * normalised partial output and a base-2 log-sum-exp per (request, split,
+ * head); stage 2 merges the splits.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers unless stated otherwise; the
+ *     caller allocates and owns every buffer (the library allocates nothing and
+ *     keeps no state between calls; calls on different streams with disjoint
+ *     outputs and workspaces may run concurrently).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; nothing synchronises with the host.
+ *   - Return value: MLA_OK (0) or a negative MLA_ERR_* code.  Argument errors
+ *     are detected on the host before anything is enqueued.  Device-resident
+ *     contents (indptr monotonicity, page ids in range) are not inspected on
+ *     the hot path: out-of-range page ids are undefined behaviour, exactly as
+ *     for an out-of-range pointer.
+ *   - bf16 values are raw IEEE bfloat16 bit patterns (uint16).
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+/* Fixed MLA geometry (page 668813 module constants). */
+#define MLA_NUM_HEADS 16
+#define MLA_HEAD_DIM_QK 576      /* 512 latent + 64 rope */
+#define MLA_HEAD_DIM_V 512       /* V = first 512 latent dims */
+#define MLA_MXFP4_ROW_BYTES 288  /* 576 e2m1 codes, two per byte */
+#define MLA_MXFP4_ROW_SCALES 18  /* one e8m0 per 32 elements */
+
+/* Element formats. */
+#define MLA_DTYPE_BF16 0         /* IEEE bfloat16 */
+#define MLA_DTYPE_FP8_E4M3FN 1   /* OCP fp8 e4m3fn with one fp32 per-tensor scale */
+#define MLA_DTYPE_MXFP4 2        /* OCP MX e2m1 + e8m0 per 32 elements */
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MLA_ERR_DTYPE (-2)       /* unsupported (q, kv) format pair */
+#define MLA_ERR_ARG (-3)         /* a size/count is out of range */
+#define MLA_ERR_ALIGN (-4)       /* a buffer is not 16-byte aligned */
+#define MLA_ERR_WORKSPACE (-5)   /* workspace missing or too small */
+#define MLA_ERR_LAUNCH (-6)      /* the HIP runtime rejected a launch */
+#define MLA_ERR_DEVICE (-7)      /* no usable gfx950 device */
+
+#define MLA_MAX_SPLITS 256
+
+/*
+ * mla_decode - split-K MLA decode of `batch` single-token requests.
+ *
+ * q          [batch,16,576] bf16            (q_dtype = MLA_DTYPE_BF16), or
+ *            [batch,16,576] e4m3fn bytes    (q_dtype = MLA_DTYPE_FP8_E4M3FN), or
+ *            [batch,16,288] packed e2m1     (q_dtype = MLA_DTYPE_MXFP4).
+ * q_scale    NULL for bf16; device float[1] per-tensor scale for fp8 (the value
+ *            a code is multiplied by); device uint8 e8m0 [batch*16, 18] for mxfp4.
+ * kv_cache   physical cache rows: [num_kv_rows,576] bf16 | [num_kv_rows,576]
+ *            e4m3fn | [num_kv_rows,288] packed e2m1 (byte i: element 2i in the
+ *            low nibble, 2i+1 in the high nibble; page 668813's stage-1 kernel).
+ * kv_scale   NULL for bf16; device float[1] for fp8; device uint8 e8m0
+ *            [num_kv_rows,18] for mxfp4, whose allocation must cover at least
+ *            ceil(18*num_kv_rows/16)*16 bytes (rows are read as aligned dwords).
+ * kv_indptr  device int32[batch+1], token offsets: request b has
+ *            kv_indptr[b+1]-kv_indptr[b] >= 0 tokens.
+ * page_table device int32 physical page ids.
+ * page_indptr NULL: one table over the concatenated token stream - token t of
+ *            request b is logical position g = kv_indptr[b] + t and lives in row
+ *            page_table[g / page_size] * page_size + g % page_size.
+ *            Non-NULL (device int32[batch]): per-request tables - token t of
+ *            request b lives in row page_table[page_indptr[b] + t / page_size]
+ *            * page_size + t % page_size.
+ * page_size  >= 1 rows per page.
+ * num_splits 1..MLA_MAX_SPLITS chunks per request (ceil(L/S) tokens each, the
+ *            last ones possibly short or empty).  1 writes `out` directly from
+ *            stage 1 and needs no workspace.
+ * out        [batch,16,512] bf16, round-to-nearest-even of the fp32 result.
+ * workspace  device scratch of at least mla_workspace_bytes(batch, num_splits)
+ *            bytes (may be NULL when that is 0); contents on entry are ignored.
+ *
+ * Supported (q, kv) pairs: (bf16,bf16), (bf16,fp8), (fp8,fp8), (bf16,mxfp4),
+ * (mxfp4,mxfp4); anything else returns MLA_ERR_DTYPE.  q, kv_cache, out and
+ * workspace must be 16-byte aligned.
+ */
+int mla_decode(const void* q, int32_t q_dtype, const void* q_scale,
+               const void* kv_cache, int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows,
+               const int32_t* kv_indptr, int32_t batch,
+               const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+               int32_t num_splits, void* out, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * mla_validate - the host-side argument checks of mla_decode, with the same
+ * arguments, returning the status mla_decode would return before launching.
+ * Makes no HIP call and touches no device memory (usable without a GPU).
+ */
+int mla_validate(const void* q, int32_t q_dtype, const void* q_scale,
+                 const void* kv_cache, int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows,
+                 const int32_t* kv_indptr, int32_t batch,
+                 const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                 int32_t num_splits, void* out, void* workspace, size_t workspace_bytes);
+
+/* Bytes of workspace mla_decode needs: fp32 partial outputs [batch,S,16,512]
+ * plus base-2 log-sum-exps [batch,S,16]; 0 when num_splits == 1.  Returns 0
+ * for invalid arguments too (batch < 1 or num_splits outside 1..MLA_MAX_SPLITS). */
+size_t mla_workspace_bytes(int32_t batch, int32_t num_splits);
+
+/*
+ * mla_choose_num_splits - split count for `batch` requests of about
+ * `kv_len` tokens on a device with `num_cus` compute units (0 = 256, MI355X).
+ * Occupancy model: aim for batch*S close to a whole number of waves of
+ * one-workgroup-per-CU, keep at least 256 tokens per split, and keep the
+ * stage-2 partial traffic small; see the design notes for the calibration.
+ * (Page 695854's split selectors and page 668813's split tables pick S per
+ * shape for the same reasons.)  Returns a value in 1..MLA_MAX_SPLITS.
+ */
+int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, int32_t num_cus);
+
+/* mla_recommend_page_size - page size for a cache serving `batch` requests
+ * of about `kv_len` tokens (page 668813's page-size table and page 600081's
+ * selector use 1 for short and 8 for long sequences); the kernels accept any
+ * page size >= 1. */
+int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len);
+
+/*
+ * mla_quantize_fp8 - OCP e4m3fn per-tensor quantisation of n bf16 values
+ * (page 668813, the naive per-tensor fp8 quantiser): with dynamic != 0 the
+ * scale is max(max|x|, 1e-12) / 448 computed on the device and written to
+ * *scale (device float[1]); with dynamic == 0 *scale is read as given.  Each
+ * code is the nearest e4m3fn value to clamp(x / scale, -448, 448) (fp32
+ * division, ties to even).  NaN inputs are ignored by the amax.
+ */
+int mla_quantize_fp8(const void* src_bf16, int64_t n, uint8_t* dst, float* scale, int32_t dynamic,
+                     void* stream);
+
+/*
+ * mla_quantize_mxfp4 - OCP MX mxfp4 quantisation of rows of `cols` bf16 values
+ * (cols a positive multiple of 32): per 32-element block the e8m0 scale is
+ * floor(log2(amax)) - 2 + 127 clamped to [0,254] (0 for an all-zero block) and
+ * each element is the nearest e2m1 value to x / 2^(e-127), ties to even,
+ * saturating at +-6.  packed: [rows, cols/2] (element 2i in the low nibble);
+ * scales: [rows, cols/32].
+ */
+int mla_quantize_mxfp4(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* packed,
+                       uint8_t* scales, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* mla_status_string(int status);
+
+/* MLA_ABI_VERSION of the loaded library. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_DECODE_H_ */

@@ -1,0 +1,225 @@
+"""Python binding of the MI355X MLA decode library (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of
+``csrc/mla_decode.hip`` behind the C ABI declared in ``include/mla_decode.h``;
+this module only checks tensor placement, picks the format codes from tensor
+dtypes, passes raw pointers and the current HIP stream through ctypes, and
+allocates outputs/workspaces with torch.  There is no fallback: if the shared
+library is missing the calls raise.
+
+Tensor conventions:
+  bf16 data          torch.bfloat16
+  fp8 e4m3fn data    torch.float8_e4m3fn (one fp32 per-tensor scale, a 1-element
+                     float32 tensor on the device)
+  mxfp4 data         torch.uint8 packed [..., 288] + torch.uint8 e8m0 scales [..., 18]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+__all__ = [
+    "BF16", "FP8", "MXFP4", "HEADS", "D_QK", "D_V",
+    "load", "decode", "workspace_bytes", "choose_num_splits", "recommend_page_size",
+    "quantize_fp8", "quantize_mxfp4", "validate", "status_string", "StatusError",
+    "mxfp4_scale_buffer",
+]
+
+BF16, FP8, MXFP4 = 0, 1, 2
+HEADS, D_QK, D_V = 16, 576, 512
+MXFP4_ROW_BYTES, MXFP4_ROW_SCALES = 288, 18
+MAX_SPLITS = 256
+
+_lock = threading.Lock()
+_lib = None
+
+_c_int32, _c_int64, _c_size, _c_void = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+_DECODE_ARGS = [_c_void, _c_int32, _c_void, _c_void, _c_int32, _c_void, _c_int64, _c_void, _c_int32,
+                _c_void, _c_void, _c_int32, _c_int32, _c_void, _c_void, _c_size]
+
+EXPORTS = ("mla_decode", "mla_validate", "mla_workspace_bytes", "mla_choose_num_splits",
+           "mla_recommend_page_size", "mla_quantize_fp8", "mla_quantize_mxfp4", "mla_status_string",
+           "mla_abi_version")
+
+
+class StatusError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def load():
+    """Load (without building) the in-tree shared library."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = _build.LIB_PATH
+            if not os.path.exists(path):
+                raise RuntimeError(f"{path} is missing: run __graft_entry__.build() (or "
+                                   f"python -m mla_latent_kv_13_amd.build) first")
+            L = ctypes.CDLL(path)
+            L.mla_decode.restype = ctypes.c_int
+            L.mla_decode.argtypes = _DECODE_ARGS + [_c_void]
+            L.mla_validate.restype = ctypes.c_int
+            L.mla_validate.argtypes = _DECODE_ARGS
+            L.mla_workspace_bytes.restype = _c_size
+            L.mla_workspace_bytes.argtypes = [_c_int32, _c_int32]
+            L.mla_choose_num_splits.restype = _c_int32
+            L.mla_choose_num_splits.argtypes = [_c_int32, _c_int32, _c_int32, _c_int32]
+            L.mla_recommend_page_size.restype = _c_int32
+            L.mla_recommend_page_size.argtypes = [_c_int32, _c_int32]
+            L.mla_quantize_fp8.restype = ctypes.c_int
+            L.mla_quantize_fp8.argtypes = [_c_void, _c_int64, _c_void, _c_void, _c_int32, _c_void]
+            L.mla_quantize_mxfp4.restype = ctypes.c_int
+            L.mla_quantize_mxfp4.argtypes = [_c_void, _c_int64, _c_int64, _c_void, _c_void, _c_void]
+            L.mla_status_string.restype = ctypes.c_char_p
+            L.mla_status_string.argtypes = [ctypes.c_int]
+            L.mla_abi_version.restype = _c_int32
+            L.mla_abi_version.argtypes = []
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().mla_status_string(int(status)).decode()
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _fmt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8
+    if t.dtype == torch.uint8:
+        return MXFP4
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+
+
+def workspace_bytes(batch: int, num_splits: int) -> int:
+    return int(load().mla_workspace_bytes(int(batch), int(num_splits)))
+
+
+def choose_num_splits(batch: int, kv_len: int, kv_dtype: int, num_cus: int = 0) -> int:
+    return int(load().mla_choose_num_splits(int(batch), int(kv_len), int(kv_dtype), int(num_cus)))
+
+
+def recommend_page_size(batch: int, kv_len: int) -> int:
+    return int(load().mla_recommend_page_size(int(batch), int(kv_len)))
+
+
+def _decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale, kv_scale,
+                 page_indptr, out, workspace):
+    batch = kv_indptr.numel() - 1
+    num_rows = kv_cache.shape[0] if kv_cache.dim() else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return [_ptr(q), _fmt(q), _ptr(q_scale), _ptr(kv_cache), _fmt(kv_cache), _ptr(kv_scale), num_rows,
+            _ptr(kv_indptr), batch, _ptr(page_table), _ptr(page_indptr), int(page_size), int(num_splits),
+            _ptr(out), _ptr(workspace), ws_bytes]
+
+
+def validate(q, kv_cache, kv_indptr, page_table, page_size, num_splits, *, q_scale=None, kv_scale=None,
+             page_indptr=None, out=None, workspace=None) -> int:
+    """Host-side argument check (no GPU work); returns the status code."""
+    return int(load().mla_validate(*_decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits,
+                                                 q_scale, kv_scale, page_indptr, out, workspace)))
+
+
+def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Tensor,
+           page_size: int, num_splits: int | None = None, *, q_scale=None, kv_scale=None,
+           page_indptr=None, out=None, workspace=None, kv_len_hint: int | None = None, stream=None):
+    """MLA decode; returns out [batch,16,512] bf16 (enqueued on the current stream).
+
+    q          [B,16,576] bf16 / float8_e4m3fn, or [B,16,288] uint8 (mxfp4, with q_scale e8m0 [B*16,18])
+    kv_cache   [R,576] bf16 / float8_e4m3fn, or [R,288] uint8 (mxfp4, with kv_scale e8m0 [R,18])
+    kv_indptr  int32 [B+1] token offsets; page_table int32 page ids; page_indptr optional int32 [B]
+    """
+    batch = kv_indptr.numel() - 1
+    if num_splits is None:
+        hint = kv_len_hint if kv_len_hint is not None else max(1, kv_cache.shape[0] // max(batch, 1))
+        num_splits = choose_num_splits(batch, hint, _fmt(kv_cache))
+    if out is None:
+        out = torch.empty((batch, HEADS, D_V), dtype=torch.bfloat16, device=kv_cache.device)
+    need = workspace_bytes(batch, num_splits) if batch > 0 else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=kv_cache.device)
+    _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out, workspace)
+    rc = load().mla_decode(*_decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale,
+                                         kv_scale, page_indptr, out, workspace), _stream(stream))
+    if rc:
+        raise StatusError("mla_decode", rc)
+    return out
+
+
+def quantize_fp8(x: torch.Tensor, scale: torch.Tensor | float | None = None, stream=None):
+    """Per-tensor OCP e4m3fn quantisation of a bf16 tensor on the device.
+
+    scale None -> dynamic (max|x| / 448, computed on the device); a float or a
+    1-element float32 device tensor -> static.  Returns (codes, scale_tensor).
+    """
+    _dev(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("quantize_fp8 expects bfloat16 input")
+    dynamic = scale is None
+    if dynamic:
+        sc = torch.empty(1, dtype=torch.float32, device=x.device)
+    elif isinstance(scale, torch.Tensor):
+        sc = scale.to(device=x.device, dtype=torch.float32).reshape(1).contiguous()
+    else:
+        sc = torch.tensor([float(scale)], dtype=torch.float32, device=x.device)
+    codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    rc = load().mla_quantize_fp8(x.data_ptr(), x.numel(), codes.data_ptr(), sc.data_ptr(), int(dynamic),
+                                 _stream(stream))
+    if rc:
+        raise StatusError("mla_quantize_fp8", rc)
+    return codes, sc
+
+
+def mxfp4_scale_buffer(rows: int, device) -> torch.Tensor:
+    """An e8m0 scale array [rows, 18] whose allocation is padded to 16 bytes."""
+    n = rows * MXFP4_ROW_SCALES
+    base = torch.empty(((n + 15) // 16) * 16, dtype=torch.uint8, device=device)
+    return base[:n].view(rows, MXFP4_ROW_SCALES)
+
+
+def quantize_mxfp4(x: torch.Tensor, stream=None):
+    """OCP MX mxfp4 quantisation of a bf16 tensor [..., cols] (cols % 32 == 0).
+
+    Returns (packed uint8 [..., cols/2], e8m0 uint8 [..., cols/32]); for 576-wide
+    rows the scale array's allocation is padded as mla_decode requires.
+    """
+    _dev(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("quantize_mxfp4 expects bfloat16 input")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    packed = torch.empty(x.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=x.device)
+    nsc = rows * (cols // 32)
+    base = torch.empty(max(16, ((nsc + 15) // 16) * 16), dtype=torch.uint8, device=x.device)
+    scales = base[:nsc].view(x.shape[:-1] + (cols // 32,))
+    rc = load().mla_quantize_mxfp4(x.data_ptr(), rows, cols, packed.data_ptr(), scales.data_ptr(), _stream(stream))
+    if rc:
+        raise StatusError("mla_quantize_mxfp4", rc)
+    return packed, scales

@@ -1,0 +1,122 @@
+// Host-only half of the MLA decode library: argument validation, workspace
+// sizing, the split-count / page-size heuristic and status strings.  Nothing
+// here calls the HIP runtime or touches device memory, so all of it runs (and
+// is tested) on a machine without a GPU.
+#include <cstddef>
+#include <cstdint>
+
+#include "mla_decode.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_pair(int32_t qd, int32_t kd) {
+  if (kd == MLA_DTYPE_BF16) return qd == MLA_DTYPE_BF16;
+  if (kd == MLA_DTYPE_FP8_E4M3FN) return qd == MLA_DTYPE_BF16 || qd == MLA_DTYPE_FP8_E4M3FN;
+  if (kd == MLA_DTYPE_MXFP4) return qd == MLA_DTYPE_BF16 || qd == MLA_DTYPE_MXFP4;
+  return false;
+}
+
+// KV bytes per cache row (scales included) - the dominant stream of stage 1.
+int64_t kv_row_bytes(int32_t kd) {
+  switch (kd) {
+    case MLA_DTYPE_BF16: return 2 * MLA_HEAD_DIM_QK;
+    case MLA_DTYPE_FP8_E4M3FN: return MLA_HEAD_DIM_QK;
+    default: return MLA_MXFP4_ROW_BYTES + MLA_MXFP4_ROW_SCALES;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_DTYPE: return "unsupported (q, kv) element format pair";
+    case MLA_ERR_ARG: return "a size or count is out of range";
+    case MLA_ERR_ALIGN: return "a buffer is not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case MLA_ERR_DEVICE: return "no usable gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+size_t mla_workspace_bytes(int32_t batch, int32_t num_splits) {
+  if (batch < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return 0;
+  if (num_splits == 1) return 0;
+  const size_t parts = static_cast<size_t>(batch) * static_cast<size_t>(num_splits) * MLA_NUM_HEADS;
+  // partial outputs first (16-byte aligned rows), then the log-sum-exps
+  return parts * MLA_HEAD_DIM_V * sizeof(float) + parts * sizeof(float);
+}
+
+int mla_validate(const void* q, int32_t q_dtype, const void* q_scale, const void* kv_cache,
+                 int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows,
+                 const int32_t* kv_indptr, int32_t batch, const int32_t* page_table,
+                 const int32_t* page_indptr, int32_t page_size, int32_t num_splits, void* out,
+                 void* workspace, size_t workspace_bytes) {
+  (void)page_indptr;  // optional
+  if (batch < 0) return MLA_ERR_ARG;
+  if (page_size < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_ARG;
+  if (num_kv_rows < 0) return MLA_ERR_ARG;
+  if (static_cast<int64_t>(batch) * num_splits > 0x7fffffffLL) return MLA_ERR_ARG;
+  if (!supported_pair(q_dtype, kv_dtype)) return MLA_ERR_DTYPE;
+  if (batch == 0) return MLA_OK;  // nothing to do
+  if (!q || !kv_cache || !kv_indptr || !page_table || !out) return MLA_ERR_NULL;
+  if (q_dtype != MLA_DTYPE_BF16 && !q_scale) return MLA_ERR_NULL;
+  if (kv_dtype != MLA_DTYPE_BF16 && !kv_scale) return MLA_ERR_NULL;
+  if (num_kv_rows < 1) return MLA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if (kv_dtype == MLA_DTYPE_MXFP4 && !aligned16(kv_scale)) return MLA_ERR_ALIGN;
+  if (kv_dtype == MLA_DTYPE_FP8_E4M3FN && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)) return MLA_ERR_ALIGN;
+  if (q_dtype == MLA_DTYPE_FP8_E4M3FN && (reinterpret_cast<uintptr_t>(q_scale) & 3u)) return MLA_ERR_ALIGN;
+  const size_t need = mla_workspace_bytes(batch, num_splits);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  }
+  return MLA_OK;
+}
+
+int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, int32_t num_cus) {
+  if (batch < 1 || kv_len < 1) return 1;
+  if (num_cus <= 0) num_cus = 256;
+  if (kv_dtype < MLA_DTYPE_BF16 || kv_dtype > MLA_DTYPE_MXFP4) kv_dtype = MLA_DTYPE_FP8_E4M3FN;
+  // Cost in "bytes streamed by the busiest CU": stage 1 runs in
+  // ceil(batch*S / num_cus) rounds of one workgroup per CU, each streaming
+  // its chunk rounded up to 128 tokens (four waves x 32-token sub-tiles);
+  // S > 1 adds the partial outputs (written and re-read, spread over the
+  // CUs) and a fixed second launch worth ~3 us of per-CU bandwidth.
+  const double row = static_cast<double>(kv_row_bytes(kv_dtype));
+  const double launch_bytes = 3.0e-6 * 8.0e12 / 256.0;
+  const int32_t max_s = kv_len / 32 < 1 ? 1 : (kv_len / 32 > MLA_MAX_SPLITS ? MLA_MAX_SPLITS : kv_len / 32);
+  double best = 0.0;
+  int32_t best_s = 1;
+  for (int32_t s = 1; s <= max_s; ++s) {
+    const int64_t chunk = (static_cast<int64_t>(kv_len) + s - 1) / s;
+    const int64_t chunk_eff = (chunk + 127) / 128 * 128;
+    const int64_t rounds = (static_cast<int64_t>(batch) * s + num_cus - 1) / num_cus;
+    double cost = static_cast<double>(rounds) * static_cast<double>(chunk_eff) * row;
+    if (s > 1) {
+      const double partial = static_cast<double>(batch) * s * MLA_NUM_HEADS * (MLA_HEAD_DIM_V + 1) * 4.0 * 2.0;
+      cost += partial / num_cus + launch_bytes;
+    }
+    if (s == 1 || cost < best * 0.999) {
+      best = cost;
+      best_s = s;
+    }
+  }
+  return best_s;
+}
+
+int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len) {
+  (void)batch;
+  return kv_len > 1024 ? 8 : 1;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs for MLA decode (shared by tests, smoke and bench).
+
+This module only draws random numbers and lays out index arrays; it holds none
+of the method's arithmetic (no quantisation, no attention).  Both the HIP path
+and the CPU oracle consume what it produces, each applying its own quantiser.
+
+Distributions follow the workloads the pages were tuned on: Q and the latent
+cache rows are N(0,1), rounded to bfloat16 (page 600081 notes that q is
+standard normal in the task's input generator); caches are paged with a seeded
+random permutation of physical pages where the workload says so.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+HEADS, D_QK = 16, 576
+BASE_SEED = 20261202
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    kv_len: int
+    q_fmt: str          # "bf16" | "fp8" | "mxfp4"
+    kv_fmt: str         # "bf16" | "fp8" | "mxfp4"
+    page_size: int
+    shuffle: bool
+    num_splits: int | None  # None: the library heuristic picks it
+    q_scale: float | None = None  # static fp8 Q scale
+    index: int = 0
+
+
+# The five benchmark shapes (bs x kv_len x precision mix) plus the bs=256 fp8
+# shape at which the 70%-of-HBM-peak target is stated.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("bs4_kv1024_bf16", 4, 1024, "bf16", "bf16", 1, False, None, None, 0),
+        Workload("bs32_kv1024_a16w8", 32, 1024, "bf16", "fp8", 1, False, 8, None, 1),
+        Workload("bs4_kv8192_a8w8", 4, 8192, "fp8", "fp8", 8, True, 32, 6.0 / 448.0, 2),
+        Workload("bs64_kv8192_a16w8", 64, 8192, "bf16", "fp8", 8, True, 8, None, 3),
+        Workload("bs256_kv8192_mxfp4", 256, 8192, "bf16", "mxfp4", 8, True, 2, None, 4),
+        Workload("bs256_kv8192_mxfp4_q4", 256, 8192, "mxfp4", "mxfp4", 8, True, 2, None, 5),
+        Workload("bs256_kv8192_a16w8", 256, 8192, "bf16", "fp8", 8, True, None, None, 6),
+    ]
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def normal_bf16(shape, seed: int, device="cpu", std: float = 1.0) -> torch.Tensor:
+    """N(0, std^2) drawn in fp32 with a seeded generator, rounded to bf16."""
+    g = _gen(seed, device)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(torch.bfloat16)
+
+
+def make_case(batch: int, lengths, page_size: int, *, shuffle: bool, seed: int, device="cpu",
+              per_request_pages: bool = False, extra_pages: int = 0):
+    """Q, a paged bf16 latent cache and its index arrays.
+
+    lengths            int or list of per-request token counts (may contain 0)
+    per_request_pages  False: one page table over the concatenated token stream
+                       (kv_indptr are token offsets into it); True: each request
+                       owns ceil(L/P) pages starting at page_indptr[b].
+    extra_pages        unused physical pages appended (they hold random data too)
+    Returns a dict of tensors on `device`: q [B,16,576] bf16, kv [R,576] bf16,
+    kv_indptr int32 [B+1], page_table int32, page_indptr int32 [B] or None.
+    """
+    if isinstance(lengths, int):
+        lengths = [lengths] * batch
+    assert len(lengths) == batch
+    kv_indptr = [0]
+    for L in lengths:
+        kv_indptr.append(kv_indptr[-1] + int(L))
+    total = kv_indptr[-1]
+    if per_request_pages:
+        npg = [math.ceil(L / page_size) for L in lengths]
+        page_indptr = [0]
+        for c in npg[:-1]:
+            page_indptr.append(page_indptr[-1] + c)
+        used = sum(npg)
+    else:
+        page_indptr = None
+        used = math.ceil(total / page_size) if total else 0
+    num_pages = max(1, used + extra_pages)
+    if shuffle:
+        perm = torch.randperm(num_pages, generator=_gen(seed + 1000, "cpu"))
+    else:
+        perm = torch.arange(num_pages)
+    q = normal_bf16((batch, HEADS, D_QK), seed, device)
+    kv = normal_bf16((num_pages * page_size, D_QK), seed + 1, device)
+    return {
+        "q": q,
+        "kv": kv,
+        "kv_indptr": torch.tensor(kv_indptr, dtype=torch.int32, device=device),
+        "page_table": perm[: max(used, 1)].to(torch.int32).to(device).contiguous(),
+        "page_indptr": None if page_indptr is None else torch.tensor(page_indptr, dtype=torch.int32, device=device),
+        "page_size": page_size,
+        "lengths": list(lengths),
+    }
+
+
+def workload_case(w: Workload, device="cpu", seed_offset: int = 0):
+    """The synthetic instance of a named workload (seed = base + index)."""
+    return make_case(w.batch, w.kv_len, w.page_size, shuffle=w.shuffle, seed=BASE_SEED + w.index + seed_offset,
+                     device=device)

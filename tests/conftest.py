@@ -1,0 +1,19 @@
+import os
+import sys
+
+import pytest
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    oracle.lib()  # builds oracle/_build/liboracle.so with gcc if it is not there yet
+    return oracle
