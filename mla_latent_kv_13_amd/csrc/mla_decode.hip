@@ -1,0 +1,881 @@
+// MI355X (gfx950 / CDNA4) kernels for single-token MLA decode and the
+// C-ABI entry points that launch them.
+//
+// Method (kernelindex.com "kernelbot-amd-mixed-mla-668813": the mxfp4 stage-1
+// kernel and its log2 stage-2 combine; "...-695854": the fp8 single-pass,
+// split and reduce kernels and the torch fallback that states the plain math):
+// 16 query heads attend over one latent KV head of width 576; V is the first
+// 512 latent dims; the logit scale is 1/sqrt(576).  Stage 1 handles one
+// (request, split) per workgroup; stage 2 merges the splits.
+//
+// Stage-1 design (one workgroup = 4 independent waves):
+//   * A split's tokens are cut into 32-token sub-tiles dealt round-robin to the
+//     waves.  Each wave streams its sub-tiles HBM -> LDS with direct-to-LDS
+//     16-byte loads (global_load_lds_dwordx4) into a private ring of NBUF
+//     slots, the page table being gathered by the same asynchronous path one
+//     or two sub-tiles ahead, and waits with explicit vmcnt counts so several
+//     sub-tiles stay in flight while it computes.
+//   * QK^T runs on MFMA with the 16 heads as the N=16 side: s^T = K * Q^T,
+//     Q held in registers as the B operand.  bf16 x bf16 and bf16 x fp8 (fp8
+//     widened exactly to bf16) use v_mfma_f32_16x16x32_bf16; fp8 x fp8 and
+//     mxfp4 x mxfp4 use v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales for
+//     fp8, the e8m0 block scales for mxfp4).
+//   * Online softmax in the log2 domain.  The QK accumulator layout puts one
+//     head per lane, so the running max / sum are per-lane scalars and the
+//     P tile is already the B operand of P*V (no LDS round trip).
+//   * P*V as O^T = V^T * P^T on v_mfma_f32_16x16x32_bf16, V taken from the
+//     SAME staged tile (no second HBM read): transposing LDS reads
+//     (ds_read_b64_tr_b16 / _b8) for bf16 / fp8, per-token e2m1->bf16
+//     conversion plus register shuffles for mxfp4.
+//   * The four waves merge their (max, sum, O) through LDS at the end; S == 1
+//     writes bf16 out directly, otherwise fp32 partial O / base-2 LSE.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <utility>
+
+#include "mla_decode.h"
+
+namespace {
+
+constexpr int kHeads = 16;
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSub = 32;  // tokens per wave sub-tile
+
+constexpr int FBF16 = MLA_DTYPE_BF16;
+constexpr int FFP8 = MLA_DTYPE_FP8_E4M3FN;
+constexpr int FMX = MLA_DTYPE_MXFP4;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// ------------------------------------------------------------------ layout
+// Per-format cache row geometry and ring depth.
+template <int KF> struct Kv;
+template <> struct Kv<FBF16> {
+  static constexpr int kRow = 2 * kDqk;  // bytes per cache row
+  static constexpr int kUnits = kRow / 16;
+  static constexpr int kNdmaX4 = kUnits / 2;  // 64 lanes x 16 B = 2 units of 32 tokens
+  static constexpr int kNdmaSc = 0;
+  static constexpr int kNbuf = 1;
+};
+template <> struct Kv<FFP8> {
+  static constexpr int kRow = kDqk;
+  static constexpr int kUnits = kRow / 16;
+  static constexpr int kNdmaX4 = kUnits / 2;
+  static constexpr int kNdmaSc = 0;
+  static constexpr int kNbuf = 2;
+};
+template <> struct Kv<FMX> {
+  static constexpr int kRow = MLA_MXFP4_ROW_BYTES;
+  static constexpr int kUnits = kRow / 16;
+  static constexpr int kNdmaX4 = kUnits / 2;
+  static constexpr int kNdmaSc = 3;  // 32 tokens x 5 aligned dwords = 160 lanes
+  static constexpr int kNbuf = 3;
+};
+
+template <int KF> struct Lay {
+  static constexpr int kNbuf = Kv<KF>::kNbuf;
+  static constexpr int kSlot = Kv<KF>::kUnits * 512;           // 32 tokens x row
+  static constexpr int kScSlot = Kv<KF>::kNdmaSc ? 768 : 0;     // 3 x 64 dwords
+  static constexpr int kParSlot = Kv<KF>::kNdmaSc ? 32 : 0;     // row parity per token
+  static constexpr int kD = kNbuf > 1 ? kNbuf - 1 : 1;          // page-id prefetch distance
+  static constexpr int kNpid = kD + 1;
+  static constexpr int kPidSlot = 256;                          // 64 lanes x 4 B
+  static constexpr int kScOff = kNbuf * kSlot;
+  static constexpr int kParOff = kScOff + kNbuf * kScSlot;
+  static constexpr int kPidOff = kParOff + kNbuf * kParSlot;
+  static constexpr int kWaveBytes = kPidOff + kNpid * kPidSlot;
+  static constexpr int kCombine = 2 * 128 * 64 * 4 + 2 * kWaves * kHeads * 4;
+  static constexpr int kTotal = kWaves * kWaveBytes > kCombine ? kWaves * kWaveBytes : kCombine;
+  static constexpr int kNdma = Kv<KF>::kNdmaX4 + Kv<KF>::kNdmaSc;  // VMEM instrs per sub-tile
+};
+
+// Byte offset, inside a slot, of 16-byte unit k of sub-tile token t (0..31).
+// Units are stored [k/2][k%2][slot]: one DMA instruction fills units 2i, 2i+1
+// of all 32 tokens.  The slot index is swizzled so that the QK reads (8 rows
+// of one unit), the transposing P*V reads (8 tokens of one unit) and the bf16
+// pairs of units all land on distinct banks.
+__device__ __forceinline__ int swz(int t) { return t ^ ((t >> 2) & 4); }
+__device__ __forceinline__ int unit_off(int t, int k) {
+  return 1024 * (k >> 1) + 512 * (k & 1) + 16 * (swz(t) ^ ((k & 1) << 2));
+}
+
+// ------------------------------------------------------------- primitives
+template <class T>
+__device__ __forceinline__ T lds_ld(int off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(static_cast<uintptr_t>(off));
+}
+template <class T>
+__device__ __forceinline__ void lds_st(int off, T v) {
+  *reinterpret_cast<__attribute__((address_space(3))) T*>(static_cast<uintptr_t>(off)) = v;
+}
+
+// Direct-to-LDS loads.  LDS address = m0 + offset + 16*lane (x4) or 4*lane (dword);
+// the immediate offset is added to the global address as well.
+template <int OFF>
+__device__ __forceinline__ void dma_x4(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+               :
+               : "v"(g), "s"(m0), "n"(OFF)
+               : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
+template <int... I>
+__device__ __forceinline__ void dma_tile(const char* g, uint32_t m0, std::integer_sequence<int, I...>) {
+  (dma_x4<32 * I>(g, m0 + 992u * I), ...);
+}
+
+__device__ __forceinline__ float e8m0_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+__device__ __forceinline__ uint32_t bits(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// bf16 pair (lo = low half of x, hi = low half of y) and the same for high halves
+__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return (x & 0xffffu) | (y << 16); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8_t cvt_fp8x8(i32x2_t v) {
+  u32x4_t r;
+  r.x = bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
+  r.y = bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
+  r.z = bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
+  r.w = bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+// eight e2m1 codes (one dword) times a block scale -> 8 bf16
+__device__ __forceinline__ bf16x8_t cvt_fp4x8(uint32_t v, float sc) {
+  u32x4_t r;
+  r.x = bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 0));
+  r.y = bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 1));
+  r.z = bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 2));
+  r.w = bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 3));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_fp8(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ f32x4_t mfma_fp4(i32x4_t a, uint32_t sa, i32x4_t b, uint32_t sb, f32x4_t c) {
+  i32x8_t A = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  i32x8_t B = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
+
+// ------------------------------------------------------------- arguments
+struct Stage1Args {
+  const void* q;
+  const void* q_scale;
+  const char* kv;
+  const void* kv_scale;
+  const int32_t* kv_indptr;
+  const int32_t* page_table;
+  const int32_t* page_indptr;
+  float* part_o;
+  float* part_lse;
+  uint16_t* out;
+  int32_t page_size;
+  int32_t num_splits;
+  float sm_scale_log2e;
+};
+
+// Number of QK MFMA "B operands" (Q fragments) a lane holds, per format pair.
+template <int QF, int KF> struct QFrag;
+template <> struct QFrag<FBF16, FBF16> { static constexpr int kN = 18; };
+template <> struct QFrag<FBF16, FFP8> { static constexpr int kN = 18; };
+template <> struct QFrag<FBF16, FMX> { static constexpr int kN = 18; };
+template <> struct QFrag<FFP8, FFP8> { static constexpr int kN = 5; };
+template <> struct QFrag<FMX, FMX> { static constexpr int kN = 5; };
+
+// First latent dim of the 8 bf16 values that QK MFMA m takes from lane group g,
+// for bf16 Q (the permutation mirrors how the K operand is read from LDS).
+template <int KF>
+__device__ __forceinline__ int qdim_bf16(int m, int g) {
+  if constexpr (KF == FBF16) return 32 * m + 8 * g;
+  else if constexpr (KF == FFP8) return 64 * (m >> 1) + 16 * g + 8 * (m & 1);
+  else return m < 16 ? 128 * (m >> 2) + 32 * g + 8 * (m & 3) : 512 + 32 * (m - 16) + 8 * g;
+}
+
+// ------------------------------------------------------------------ stage 1
+template <int QF, int KF>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void stage1_kernel(Stage1Args a) {
+  using L = Lay<KF>;
+  constexpr int NBUF = L::kNbuf;
+  constexpr int D = L::kD;
+  constexpr int NDMA = L::kNdma;
+  constexpr int ROW = Kv<KF>::kRow;
+  __shared__ __attribute__((aligned(1024))) char smem[L::kTotal];
+  const uint32_t smem0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem));
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;   // MFMA lane group
+  const int hq = lane & 15;  // head (QK / PV output column of the 16-wide side)
+  const int S = a.num_splits;
+  const int b = blockIdx.x / S;
+  const int s = blockIdx.x - b * S;
+
+  const int kv0 = a.kv_indptr[b];
+  const int Lr = a.kv_indptr[b + 1] - kv0;
+  const int chunk = (Lr + S - 1) / S;
+  const int t0 = s * chunk;
+  const int n = max(0, min(chunk, Lr - t0));  // tokens of this split
+  const int nsub = (n + kSub - 1) / kSub;
+  const int nloc = w < nsub ? (nsub - w + kWaves - 1) / kWaves : 0;
+  const uint32_t gbase = a.page_indptr ? static_cast<uint32_t>(t0) : static_cast<uint32_t>(kv0 + t0);
+  const int32_t* ptab = a.page_table + (a.page_indptr ? a.page_indptr[b] : 0);
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+
+  // ---- Q fragments (B operands) for this lane's head
+  constexpr int NQ = QFrag<QF, KF>::kN;
+  bf16x8_t qb[QF == FBF16 ? NQ : 1];
+  i32x8_t q8[QF == FFP8 ? NQ : 1];
+  i32x4_t q4[QF == FMX ? NQ : 1];
+  uint32_t q4s[QF == FMX ? NQ : 1];
+  float qs = 1.0f, ks = 1.0f;
+  if constexpr (QF == FBF16) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qrow + qdim_bf16<KF>(m, g));
+  } else if constexpr (QF == FFP8) {
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q8[c] = *reinterpret_cast<const i32x8_t*>(qrow + 128 * c + 32 * g);
+    q8[4] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (g < 2) q8[4] = *reinterpret_cast<const i32x8_t*>(qrow + 512 + 32 * g);
+    qs = *static_cast<const float*>(a.q_scale);
+  } else {
+    const size_t qr = static_cast<size_t>(b) * kHeads + hq;
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * MLA_MXFP4_ROW_BYTES;
+    const uint8_t* qsc = static_cast<const uint8_t*>(a.q_scale) + qr * MLA_MXFP4_ROW_SCALES;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      q4[c] = *reinterpret_cast<const i32x4_t*>(qrow + 64 * c + 16 * g);
+      q4s[c] = qsc[4 * c + g];
+    }
+    q4[4] = i32x4_t{0, 0, 0, 0};
+    q4s[4] = 127u;
+    if (g < 2) {
+      q4[4] = *reinterpret_cast<const i32x4_t*>(qrow + 256 + 16 * g);
+      q4s[4] = qsc[16 + g];
+    }
+  }
+  if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
+  const float c_log2 = a.sm_scale_log2e * qs * ks;
+  const float out_mul = KF == FFP8 ? ks : 1.0f;
+  // Make the Q loads complete before the asynchronous stream starts, so the
+  // compiler's own wait for them cannot drain the in-flight tiles later.
+  if constexpr (QF == FBF16) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(qb[m]));
+  } else if constexpr (QF == FFP8) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q8[m]));
+  } else {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q4[m]), "+v"(q4s[m]));
+  }
+
+  // ---- per-wave LDS ring
+  const uint32_t wbase = smem0 + static_cast<uint32_t>(w) * L::kWaveBytes;
+  auto slot_addr = [&](int x) { return wbase + static_cast<uint32_t>(x) * L::kSlot; };
+  auto sc_addr = [&](int x) { return wbase + L::kScOff + static_cast<uint32_t>(x) * L::kScSlot; };
+  auto par_addr = [&](int x) { return wbase + L::kParOff + static_cast<uint32_t>(x) * L::kParSlot; };
+  auto pid_addr = [&](int y) { return wbase + L::kPidOff + static_cast<uint32_t>(y % L::kNpid) * L::kPidSlot; };
+
+  // DMA lane role: lane fills units 2i + hh of token tdma in every instruction i.
+  const int hh = lane >> 5;
+  const int tdma = swz((lane & 31) ^ (hh << 2));
+
+  auto issue_pid = [&](int X) {
+    const int xc = X < nloc ? X : (nloc > 0 ? nloc - 1 : 0);
+    const int tok = min(kSub * (w + kWaves * xc) + (lane & 31), max(n - 1, 0));
+    const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
+    dma_b32(ptab + gpos / P, pid_addr(X));
+  };
+  auto row_of = [&](int X, int t) -> int64_t {  // physical row of sub-tile X, token t (page id already staged)
+    const int tok = min(kSub * (w + kWaves * X) + t, n - 1);
+    const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
+    const int pid = lds_ld<int>(static_cast<int>(pid_addr(X)) + 4 * t);
+    return static_cast<int64_t>(pid) * P + gpos % P;
+  };
+  auto issue_tile = [&](int X) {
+    const int x = X % NBUF;
+    const int64_t row = row_of(X, tdma);
+    const char* gp = a.kv + row * ROW + 16 * hh;
+    if constexpr (KF == FMX) {
+      const uint8_t* ksc = static_cast<const uint8_t*>(a.kv_scale);
+      int64_t srow[3];
+      int sw[3];
+#pragma unroll
+      for (int i2 = 0; i2 < 3; ++i2) {
+        const int d = 64 * i2 + lane;
+        const int td = d < 160 ? d / 5 : 0;
+        sw[i2] = d < 160 ? d - 5 * td : 0;
+        srow[i2] = row_of(X, td);
+      }
+      wait_lgkm0();
+      dma_tile(gp, slot_addr(x), std::make_integer_sequence<int, Kv<KF>::kNdmaX4>{});
+#pragma unroll
+      for (int i2 = 0; i2 < 3; ++i2)
+        dma_b32(ksc + ((18 * srow[i2]) & ~static_cast<int64_t>(3)) + 4 * sw[i2], sc_addr(x) + 256u * i2);
+      if (hh == 0) lds_st<uint8_t>(static_cast<int>(par_addr(x)) + tdma, static_cast<uint8_t>(row & 1));
+    } else {
+      wait_lgkm0();
+      dma_tile(gp, slot_addr(x), std::make_integer_sequence<int, Kv<KF>::kNdmaX4>{});
+    }
+  };
+
+  // ---- running softmax state (head hq) and the O^T accumulators
+  f32x4_t acc[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_huge_valf();
+  float l_run = 0.0f;
+
+  // Lane-constant LDS offsets used by the reads.
+  const int tq0 = hq, tq1 = 16 + hq;  // QK A-operand rows: tokens of tile 0 / 1
+  // P*V token slots of this lane group: slot kk <-> token (kk<4 ? 4g+kk : 16+4g+kk-4)
+  auto compute = [&](int x, int ntok) {
+    const int tb = static_cast<int>(slot_addr(x));
+    // ---------------- QK^T
+    f32x4_t sacc[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int t = h2 ? tq1 : tq0;
+      f32x4_t sa = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (KF == FBF16) {
+        const int base = tb + 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(t) ^ ((g & 1) << 2));
+#pragma unroll
+        for (int m = 0; m < 18; ++m) sa = mfma_bf16(lds_ld<bf16x8_t>(base + 2048 * m), qb[m], sa);
+      } else if constexpr (KF == FFP8 && QF == FBF16) {
+        const int base = tb + 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(t) ^ ((g & 1) << 2));
+#pragma unroll
+        for (int c = 0; c < 9; ++c) {
+          const i32x4_t u = lds_ld<i32x4_t>(base + 2048 * c);
+          sa = mfma_bf16(cvt_fp8x8(i32x2_t{u.x, u.y}), qb[2 * c], sa);
+          sa = mfma_bf16(cvt_fp8x8(i32x2_t{u.z, u.w}), qb[2 * c + 1], sa);
+        }
+      } else if constexpr (KF == FFP8) {  // fp8 x fp8
+        const int be = tb + 1024 * g + 16 * swz(t);
+        const int bo = tb + 1024 * g + 512 + 16 * (swz(t) ^ 4);
+#pragma unroll
+        for (int c = 0; c < 5; ++c) {
+          i32x8_t av = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (c < 4 || g < 2) {
+            const i32x4_t u0 = lds_ld<i32x4_t>(be + 4096 * c);
+            const i32x4_t u1 = lds_ld<i32x4_t>(bo + 4096 * c);
+            av = i32x8_t{u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+          }
+          sa = mfma_fp8(av, q8[c], sa);
+        }
+      } else {  // mxfp4 K
+        const int sbase = static_cast<int>(sc_addr(x)) + 20 * t + 2 * lds_ld<uint8_t>(static_cast<int>(par_addr(x)) + t);
+        const int base = tb + 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(t) ^ ((g & 1) << 2));
+        if constexpr (QF == FBF16) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const i32x4_t u = lds_ld<i32x4_t>(base + 2048 * c);
+            const float sc = e8m0_f32(lds_ld<uint8_t>(sbase + 4 * c + g));
+            sa = mfma_bf16(cvt_fp4x8(u.x, sc), qb[4 * c + 0], sa);
+            sa = mfma_bf16(cvt_fp4x8(u.y, sc), qb[4 * c + 1], sa);
+            sa = mfma_bf16(cvt_fp4x8(u.z, sc), qb[4 * c + 2], sa);
+            sa = mfma_bf16(cvt_fp4x8(u.w, sc), qb[4 * c + 3], sa);
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t u = lds_ld<uint32_t>(tb + 8192 + 512 * e + 16 * (swz(t) ^ (e << 2)) + 4 * g);
+            const float sc = e8m0_f32(lds_ld<uint8_t>(sbase + 16 + e));
+            sa = mfma_bf16(cvt_fp4x8(u, sc), qb[16 + e], sa);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const i32x4_t u = lds_ld<i32x4_t>(base + 2048 * c);
+            const uint32_t sc = lds_ld<uint8_t>(sbase + 4 * c + g);
+            sa = mfma_fp4(u, sc, q4[c], q4s[c], sa);
+          }
+          i32x4_t ur = {0, 0, 0, 0};
+          uint32_t scr = 127u;
+          if (g < 2) {
+            ur = lds_ld<i32x4_t>(tb + 8192 + 512 * g + 16 * (swz(t) ^ (g << 2)));
+            scr = lds_ld<uint8_t>(sbase + 16 + g);
+          }
+          sa = mfma_fp4(ur, scr, q4[4], q4s[4], sa);
+        }
+      }
+      sacc[h2] = sa;
+    }
+    // ---------------- online softmax (log2 domain); lane holds head hq,
+    // tokens 4g+r (tile 0) and 16+4g+r (tile 1)
+    float sv[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = (4 * g + r < ntok) ? sacc[0][r] * c_log2 : -__builtin_huge_valf();
+      sv[4 + r] = (16 + 4 * g + r < ntok) ? sacc[1][r] * c_log2 : -__builtin_huge_valf();
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmax3(mx, sv[i]);
+    mx = fmax3(mx, __shfl_xor(mx, 16));
+    mx = fmax3(mx, __shfl_xor(mx, 32));
+    const float m_new = fmax3(m_run, mx);
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) acc[c] *= alpha;
+      m_run = m_new;
+    }
+    u32x4_t pw;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2_t pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i] - m_run)),
+                           static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i + 1] - m_run))};
+      psum += static_cast<float>(pr.x) + static_cast<float>(pr.y);
+      pw[i] = bits(pr);
+    }
+    l_run += psum;
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+    // ---------------- P*V
+    if constexpr (KF == FBF16) {
+      const int j = lane & 15;
+      const int kb = (j & 3) >> 1;
+      const int ta = 4 * g + (j >> 2), tc = 16 + 4 * g + (j >> 2);
+      const int ba = tb + 512 * kb + 16 * (swz(ta) ^ (kb << 2)) + 8 * (j & 1);
+      const int bc = tb + 512 * kb + 16 * (swz(tc) ^ (kb << 2)) + 8 * (j & 1);
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(static_cast<uintptr_t>(ba + 1024 * c)));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(static_cast<uintptr_t>(bc + 1024 * c)));
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[c] = mfma_bf16(av, pb, acc[c]);
+      }
+    } else if constexpr (KF == FFP8) {
+      const int j = lane & 15;
+      const int kk = j >> 1;
+      const int tv = kk < 4 ? 4 * g + kk : 16 + 4 * g + (kk - 4);
+      const int be = tb + 16 * swz(tv) + 8 * (j & 1);
+      const int bo = tb + 512 + 16 * (swz(tv) ^ 4) + 8 * (j & 1);
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<__attribute__((address_space(3))) i32x2_t*>(
+            static_cast<uintptr_t>((c & 1 ? bo : be) + 1024 * (c >> 1))));
+        acc[c] = mfma_bf16(cvt_fp8x8(v), pb, acc[c]);
+      }
+    } else {
+      // mxfp4: lane (column block i = lane&15) decodes unit i of its 8 tokens;
+      // output tile c row r <-> latent column 32*(4g+r) + c.
+      const int i = lane & 15;
+      const int sc0 = static_cast<int>(sc_addr(x));
+      const int pr0 = static_cast<int>(par_addr(x));
+      uint32_t vw[8][4];
+      float vsc[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int tv = kk < 4 ? 4 * g + kk : 16 + 4 * g + (kk - 4);
+        const i32x4_t u = lds_ld<i32x4_t>(tb + unit_off(tv, i));
+        vw[kk][0] = u.x;
+        vw[kk][1] = u.y;
+        vw[kk][2] = u.z;
+        vw[kk][3] = u.w;
+        vsc[kk] = e8m0_f32(lds_ld<uint8_t>(sc0 + 20 * tv + 2 * lds_ld<uint8_t>(pr0 + tv) + i));
+      }
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        uint32_t cv[8][4];  // token kk: bf16 pairs (cols 8qd + 2e, +1)
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8_t d = cvt_fp4x8(vw[kk][qd], vsc[kk]);
+          const u32x4_t du = __builtin_bit_cast(u32x4_t, d);
+          cv[kk][0] = du.x;
+          cv[kk][1] = du.y;
+          cv[kk][2] = du.z;
+          cv[kk][3] = du.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          u32x4_t av;
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            av[p] = (e & 1) ? hi_pair(cv[2 * p][e >> 1], cv[2 * p + 1][e >> 1])
+                            : lo_pair(cv[2 * p][e >> 1], cv[2 * p + 1][e >> 1]);
+          acc[8 * qd + e] = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), pb, acc[8 * qd + e]);
+        }
+      }
+    }
+  };
+
+  // ---- the asynchronous pipeline
+  if (nloc > 0) {
+#pragma unroll
+    for (int X = 0; X < D; ++X) issue_pid(X);
+    wait_vm<0>();
+    const int nfill = min(NBUF, nloc);
+    for (int X = 0; X < nfill; ++X) {
+      if (X >= D) wait_vm<D * NDMA + D - 1>();
+      issue_pid(X + D);
+      issue_tile(X);
+    }
+    for (int jx = 0; jx < nloc; ++jx) {
+      const int ahead = min(nloc - 1, jx + NBUF - 1) - jx;
+      if constexpr (NBUF == 1) {
+        wait_vm<0>();
+      } else if constexpr (NBUF == 2) {
+        if (ahead >= 1) wait_vm<NDMA + 1>();
+        else wait_vm<0>();
+      } else {
+        if (ahead >= 2) wait_vm<2 * (NDMA + 1)>();
+        else if (ahead == 1) wait_vm<NDMA + 1>();
+        else wait_vm<0>();
+      }
+      const int ubase = kSub * (w + kWaves * jx);
+      compute(jx % NBUF, min(kSub, n - ubase));
+      const int X = jx + NBUF;
+      if (X < nloc) {
+        wait_vm<D * NDMA + D - 1>();
+        issue_pid(X + D);
+        issue_tile(X);
+      }
+    }
+  }
+
+  // ---- merge the four waves (log2-domain weights), then write
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();
+  const int ob0 = static_cast<int>(smem0);
+  const int mlb = ob0 + 2 * 128 * 64 * 4;  // m[w][16], l[w][16]
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) lds_st<f32x4_t>(ob0 + buf * 32768 + (c * 64 + lane) * 16, acc[c]);
+    if (g == 0) {
+      lds_st<float>(mlb + (w * kHeads + hq) * 4, m_run);
+      lds_st<float>(mlb + (kWaves * kHeads + w * kHeads + hq) * 4, l_run);
+    }
+  };
+  auto merge = [&](int buf, int wp) {
+    const float ma = lds_ld<float>(mlb + (wp * kHeads + hq) * 4);
+    const float la = lds_ld<float>(mlb + (kWaves * kHeads + wp * kHeads + hq) * 4);
+    const float M = fmax3(ma, m_run);
+    const float fa = ma == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(ma - M);
+    const float fb = m_run == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) acc[c] = acc[c] * fb + lds_ld<f32x4_t>(ob0 + buf * 32768 + (c * 64 + lane) * 16) * fa;
+    l_run = l_run * fb + la * fa;
+    m_run = M;
+  };
+  if (w >= 2) put(w - 2);
+  __syncthreads();
+  if (w < 2) merge(w, w + 2);
+  __syncthreads();
+  if (w == 1) put(0);
+  __syncthreads();
+  if (w != 0) return;
+  merge(0, 1);
+
+  const bool nonempty = l_run > 0.0f;
+  const float mul = nonempty ? out_mul / l_run : 0.0f;
+  const float lse = nonempty ? m_run + __builtin_amdgcn_logf(l_run) : -__builtin_huge_valf();
+  const size_t orow = static_cast<size_t>(b) * kHeads + hq;
+  if (S == 1) {
+    uint16_t* op = a.out + orow * kDv;
+    if constexpr (KF == FMX) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c4 = 0; c4 < 8; ++c4) {
+          const bf16x2_t p0 = {static_cast<__bf16>(acc[4 * c4 + 0][r] * mul), static_cast<__bf16>(acc[4 * c4 + 1][r] * mul)};
+          const bf16x2_t p1 = {static_cast<__bf16>(acc[4 * c4 + 2][r] * mul), static_cast<__bf16>(acc[4 * c4 + 3][r] * mul)};
+          *reinterpret_cast<i32x2_t*>(op + 32 * (4 * g + r) + 4 * c4) = i32x2_t{static_cast<int>(bits(p0)), static_cast<int>(bits(p1))};
+        }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const bf16x2_t p0 = {static_cast<__bf16>(acc[c][0] * mul), static_cast<__bf16>(acc[c][1] * mul)};
+        const bf16x2_t p1 = {static_cast<__bf16>(acc[c][2] * mul), static_cast<__bf16>(acc[c][3] * mul)};
+        *reinterpret_cast<i32x2_t*>(op + 16 * c + 4 * g) = i32x2_t{static_cast<int>(bits(p0)), static_cast<int>(bits(p1))};
+      }
+    }
+  } else {
+    const size_t prow = (static_cast<size_t>(b) * S + s) * kHeads + hq;
+    float* po = a.part_o + prow * kDv;
+    if constexpr (KF == FMX) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c4 = 0; c4 < 8; ++c4)
+          *reinterpret_cast<f32x4_t*>(po + 32 * (4 * g + r) + 4 * c4) =
+              f32x4_t{acc[4 * c4][r], acc[4 * c4 + 1][r], acc[4 * c4 + 2][r], acc[4 * c4 + 3][r]} * mul;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4_t*>(po + 16 * c + 4 * g) = acc[c] * mul;
+    }
+    if (g == 0) a.part_lse[prow] = lse;
+  }
+}
+
+// ------------------------------------------------------------------ stage 2
+// One workgroup per (request, group of 4 heads); a thread merges 8 columns of
+// one head over the S splits with base-2 log-sum-exp weights (empty splits,
+// LSE = -inf, are skipped; an all-empty request yields zeros).
+__global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                                     uint16_t* __restrict__ out, int S) {
+  const int b = blockIdx.x >> 2;
+  const int hq = ((blockIdx.x & 3) << 2) + (threadIdx.x >> 6);
+  const int col = 8 * (threadIdx.x & 63);
+  const float* lse = part_lse + static_cast<size_t>(b) * S * kHeads + hq;
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < S; ++s) M = fmax3(M, lse[s * kHeads]);
+  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  float ws = 0.0f;
+  if (M != -__builtin_huge_valf()) {
+    for (int s = 0; s < S; ++s) {
+      const float l = lse[s * kHeads];
+      if (l == -__builtin_huge_valf()) continue;
+      const float wgt = __builtin_amdgcn_exp2f(l - M);
+      const float* po = part_o + ((static_cast<size_t>(b) * S + s) * kHeads + hq) * kDv + col;
+      a0 += *reinterpret_cast<const f32x4_t*>(po) * wgt;
+      a1 += *reinterpret_cast<const f32x4_t*>(po + 4) * wgt;
+      ws += wgt;
+    }
+  }
+  const float inv = ws > 0.0f ? 1.0f / ws : 0.0f;
+  a0 *= inv;
+  a1 *= inv;
+  u32x4_t o;
+  o.x = bits(bf16x2_t{static_cast<__bf16>(a0.x), static_cast<__bf16>(a0.y)});
+  o.y = bits(bf16x2_t{static_cast<__bf16>(a0.z), static_cast<__bf16>(a0.w)});
+  o.z = bits(bf16x2_t{static_cast<__bf16>(a1.x), static_cast<__bf16>(a1.y)});
+  o.w = bits(bf16x2_t{static_cast<__bf16>(a1.z), static_cast<__bf16>(a1.w)});
+  *reinterpret_cast<u32x4_t*>(out + (static_cast<size_t>(b) * kHeads + hq) * kDv + col) = o;
+}
+
+// -------------------------------------------------------------- quantisers
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+__global__ void zero_f32_kernel(float* p) { p[0] = 0.0f; }
+
+// max |x| over bf16 inputs, as the bit pattern of a non-negative fp32 (NaN skipped)
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t n, unsigned* __restrict__ amax) {
+  unsigned m = 0;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const unsigned a = static_cast<unsigned>(x[i] & 0x7fffu) << 16;
+    if (a <= 0x7f800000u && a > m) m = a;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned v = __shfl_xor(m, o);
+    m = v > m ? v : m;
+  }
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(amax, m);
+}
+
+__global__ void fp8_scale_kernel(float* scale) {
+  const float a = scale[0];
+  scale[0] = (a < 1e-12f ? 1e-12f : a) / 448.0f;
+}
+
+// Nearest OCP e4m3fn code to v, |v| <= 448, ties to even: with
+// e = max(floor(log2|v|), -6) the code magnitude is 8(e+6) + rne(|v| * 2^(3-e));
+// subnormals (e = -6) and the carry into the next binade fall out of the same
+// formula because the code is the concatenation exponent|mantissa.
+__device__ __forceinline__ uint8_t to_e4m3fn(float v) {
+  const float av = __builtin_fabsf(v);
+  int e = static_cast<int>((__float_as_uint(av) >> 23) & 0xff) - 127;
+  e = e < -6 ? -6 : e;
+  const int mag = 8 * (e + 6) + static_cast<int>(__builtin_rintf(__builtin_ldexpf(av, 3 - e)));
+  return static_cast<uint8_t>((__float_as_uint(v) >> 24 & 0x80u) | static_cast<unsigned>(mag));
+}
+
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ scale,
+                                                        uint8_t* __restrict__ dst) {
+  const float sc = scale[0];
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+    float q = bf16_bits_to_f32(x[i]) / sc;
+    q = q > 448.0f ? 448.0f : (q < -448.0f ? -448.0f : q);
+    dst[i] = to_e4m3fn(q);
+  }
+}
+
+// Nearest e2m1 code to v (ties to even, saturating at 6): thresholds are the
+// midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 with the tie going to the even code.
+__device__ __forceinline__ uint32_t to_e2m1(float v) {
+  const float a = __builtin_fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// one thread per 32-element block
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x, int64_t nblocks, int64_t cols,
+                                                          uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const int64_t blk = blockIdx.x * 256ll + threadIdx.x;
+  if (blk >= nblocks) return;
+  const int64_t nb = cols / 32;
+  const int64_t row = blk / nb, bi = blk - row * nb;
+  const uint16_t* xr = x + row * cols + bi * 32;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(xr + 8 * i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * i + 2 * k] = __uint_as_float(u[k] << 16);
+      v[8 * i + 2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float a = __builtin_fabsf(v[i]);
+    amax = a > amax ? a : amax;  // NaN compares false and is skipped
+  }
+  int X;
+  uint8_t sc;
+  if (amax == 0.0f) {
+    X = -127;
+    sc = 0;
+  } else {
+    X = __builtin_amdgcn_frexp_expf(amax) - 1 - 2;  // floor(log2 amax) - emax(e2m1)
+    X = X < -127 ? -127 : (X > 127 ? 127 : X);
+    sc = static_cast<uint8_t>(X + 127);
+  }
+  scales[row * nb + bi] = sc;
+  u32x4_t out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w |= to_e2m1(__builtin_ldexpf(v[8 * k + e], -X)) << (4 * e);
+    out[k] = w;
+  }
+  *reinterpret_cast<u32x4_t*>(packed + row * (cols / 2) + bi * 16) = out;
+}
+
+// ------------------------------------------------------------------ launch
+template <int QF, int KF>
+hipError_t launch_stage1(const Stage1Args& a, int batch, hipStream_t st) {
+  hipLaunchKernelGGL((stage1_kernel<QF, KF>), dim3(static_cast<unsigned>(batch) * a.num_splits), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+int grid_for(int64_t n, int per) {
+  int64_t g = (n + per - 1) / per;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return static_cast<int>(g);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode(const void* q, int32_t q_dtype, const void* q_scale, const void* kv_cache, int32_t kv_dtype,
+               const void* kv_scale, int64_t num_kv_rows, const int32_t* kv_indptr, int32_t batch,
+               const int32_t* page_table, const int32_t* page_indptr, int32_t page_size, int32_t num_splits, void* out,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = mla_validate(q, q_dtype, q_scale, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch, page_table,
+                              page_indptr, page_size, num_splits, out, workspace, workspace_bytes);
+  if (rc != MLA_OK || batch == 0) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so it is not misattributed
+  Stage1Args a;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.kv = static_cast<const char*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.kv_indptr = kv_indptr;
+  a.page_table = page_table;
+  a.page_indptr = page_indptr;
+  const size_t parts = static_cast<size_t>(batch) * num_splits * kHeads;
+  a.part_o = num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = num_splits > 1 ? static_cast<float*>(workspace) + parts * kDv : nullptr;
+  a.out = static_cast<uint16_t*>(out);
+  a.page_size = page_size;
+  a.num_splits = num_splits;
+  a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);  // log2(e) / sqrt(576)
+  hipError_t e;
+  if (kv_dtype == MLA_DTYPE_BF16) e = launch_stage1<FBF16, FBF16>(a, batch, st);
+  else if (kv_dtype == MLA_DTYPE_FP8_E4M3FN)
+    e = q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FFP8>(a, batch, st) : launch_stage1<FFP8, FFP8>(a, batch, st);
+  else e = q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FMX>(a, batch, st) : launch_stage1<FMX, FMX>(a, batch, st);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  if (num_splits > 1) {
+    hipLaunchKernelGGL(stage2_kernel, dim3(static_cast<unsigned>(batch) * 4), dim3(256), 0, st, a.part_o, a.part_lse,
+                       static_cast<uint16_t*>(out), num_splits);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+int mla_quantize_fp8(const void* src_bf16, int64_t n, uint8_t* dst, float* scale, int32_t dynamic, void* stream) {
+  if (n < 0) return MLA_ERR_ARG;
+  if (!scale) return MLA_ERR_NULL;
+  if (n > 0 && (!src_bf16 || !dst)) return MLA_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (dynamic) {
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, st, scale);
+    if (n > 0)
+      hipLaunchKernelGGL(amax_kernel, dim3(grid_for(n, 256 * 16)), dim3(256), 0, st, static_cast<const uint16_t*>(src_bf16), n,
+                         reinterpret_cast<unsigned*>(scale));
+    hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(1), 0, st, scale);
+  }
+  if (n > 0)
+    hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid_for(n, 256 * 8)), dim3(256), 0, st, static_cast<const uint16_t*>(src_bf16),
+                       n, scale, dst);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int mla_quantize_mxfp4(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* packed, uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return MLA_ERR_ARG;
+  if (rows == 0) return MLA_OK;
+  if (!src_bf16 || !packed || !scales) return MLA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(src_bf16) | reinterpret_cast<uintptr_t>(packed)) & 15u) return MLA_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int64_t nblocks = rows * (cols / 32);
+  const int64_t grid = (nblocks + 255) / 256;
+  if (grid > 0x7fffffffLL) return MLA_ERR_ARG;
+  hipLaunchKernelGGL(quant_mxfp4_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, static_cast<const uint16_t*>(src_bf16),
+                     nblocks, cols, packed, scales);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,316 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Both sides start from the same seeded bf16 inputs (mla_latent_kv_13_amd.synth)
+and quantise them with their OWN quantisers; the codes must agree bit for bit.
+Decoded outputs are then compared element by element:
+  * against the fp64 oracle on the same dequantised inputs:  |d| <= 2e-2 + 2e-2*|ref|
+    and relative L2 error <= 1e-2 (bf16 output rounding alone is ~2e-3);
+  * against the unquantised bf16 oracle:                    |d| <= 0.1 + 0.1*|ref|
+    (the tolerance page 600081 cites).
+Full-size workloads are checked on sampled (request, head) pairs that the
+oracle recomputes from the same rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_13_amd as mla
+from mla_latent_kv_13_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def bits(x):
+    return x.detach().to("cpu").to(torch.bfloat16).contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def u8(x):
+    return x.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+
+
+def check_close(out_gpu, ref, atol=2e-2, rtol=2e-2, l2=1e-2, what=""):
+    g = out_gpu.detach().to("cpu").to(torch.float64).numpy()
+    assert np.isfinite(g).all(), what
+    err = np.abs(g - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max():.4g}"
+    if l2 is not None and np.linalg.norm(ref) > 0:
+        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+        assert rel <= l2, f"{what}: relative L2 error {rel:.3g}"
+
+
+# ------------------------------------------------------------ quantisers
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fp8_quantizer_bit_exact(orc, seed):
+    x = torch.cat([synth.normal_bf16((300_001,), 100 + seed), synth.normal_bf16((999,), 200 + seed, std=1e-4),
+                   torch.tensor([0.0, -0.0, 1e-30, -3.0], dtype=torch.bfloat16)])
+    codes_g, sc_g = mla.quantize_fp8(x.to(DEV))
+    codes_o, sc_o = orc.quant_fp8(bits(x))
+    assert float(sc_g.item()) == sc_o
+    assert np.array_equal(u8(codes_g), codes_o)
+    codes_g2, _ = mla.quantize_fp8(x.to(DEV), 6.0 / 448.0)
+    codes_o2, _ = orc.quant_fp8(bits(x), float(np.float32(6.0 / 448.0)))
+    assert np.array_equal(u8(codes_g2), codes_o2)
+
+
+def test_mxfp4_quantizer_bit_exact(orc):
+    x = synth.normal_bf16((4099, 576), 300)
+    x[5] = 0.0                       # all-zero row
+    x[6, :32] = 1e-38                # tiny block
+    x[7, 40] = 1000.0                # one large element
+    x[8, 64:96] = torch.linspace(-6, 6, 32).to(torch.bfloat16)
+    p_g, s_g = mla.quantize_mxfp4(x.to(DEV))
+    p_o, s_o = orc.quant_mxfp4(bits(x))
+    assert np.array_equal(u8(s_g), s_o)
+    assert np.array_equal(u8(p_g), p_o)
+
+
+# ---------------------------------------------------------------- decode
+def prepare(case, q_fmt, kv_fmt, orc, q_static=6.0 / 448.0):
+    """GPU operands (GPU quantisers) and oracle operands (oracle quantisers); asserts equal codes."""
+    kv_g = case["kv"].to(DEV)
+    q_g = case["q"].to(DEV)
+    g = {"page_table": case["page_table"].to(DEV), "kv_indptr": case["kv_indptr"].to(DEV),
+         "page_indptr": None if case["page_indptr"] is None else case["page_indptr"].to(DEV)}
+    o = {}
+    if kv_fmt == "bf16":
+        g["kv"], g["kv_scale"] = kv_g, None
+        o.update(kv=bits(case["kv"]), kv_dtype="bf16")
+    elif kv_fmt == "fp8":
+        g["kv"], g["kv_scale"] = mla.quantize_fp8(kv_g)
+        codes, sc = orc.quant_fp8(bits(case["kv"]))
+        assert float(g["kv_scale"].item()) == sc
+        assert np.array_equal(u8(g["kv"]), codes)
+        o.update(kv=codes, kv_dtype="fp8", kv_scale=sc)
+    else:
+        g["kv"], g["kv_scale"] = mla.quantize_mxfp4(kv_g)
+        packed, e8 = orc.quant_mxfp4(bits(case["kv"]))
+        assert np.array_equal(u8(g["kv"]), packed) and np.array_equal(u8(g["kv_scale"]), e8)
+        o.update(kv=packed, kv_dtype="mxfp4", kv_e8m0=e8)
+    if q_fmt == "bf16":
+        g["q"], g["q_scale"] = q_g, None
+        o.update(q=bits(case["q"]), q_dtype="bf16")
+    elif q_fmt == "fp8":
+        g["q"], g["q_scale"] = mla.quantize_fp8(q_g, q_static)
+        codes, sc = orc.quant_fp8(bits(case["q"]), float(np.float32(q_static)))
+        assert np.array_equal(u8(g["q"]), codes)
+        o.update(q=codes, q_dtype="fp8", q_scale=sc)
+    else:
+        B = q_g.shape[0]
+        p, s = mla.quantize_mxfp4(q_g.reshape(B * 16, 576))
+        g["q"], g["q_scale"] = p.reshape(B, 16, 288), s
+        packed, e8 = orc.quant_mxfp4(bits(case["q"]).reshape(B * 16, 576))
+        assert np.array_equal(u8(p), packed) and np.array_equal(u8(s), e8)
+        o.update(q=packed.reshape(B, 16, 288), q_dtype="mxfp4", q_e8m0=e8)
+    return g, o
+
+
+def gpu_decode(case, g, S):
+    out = mla.decode(g["q"], g["kv"], g["kv_indptr"], g["page_table"], case["page_size"], S,
+                     q_scale=g["q_scale"], kv_scale=g["kv_scale"], page_indptr=g["page_indptr"])
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(case, o, orc, pairs=None):
+    return orc.decode(o["q"], o["kv"], case["kv_indptr"].cpu().numpy(), case["page_table"].cpu().numpy(),
+                      case["page_size"], q_dtype=o["q_dtype"], kv_dtype=o["kv_dtype"],
+                      q_scale=o.get("q_scale", 1.0), q_e8m0=o.get("q_e8m0"), kv_scale=o.get("kv_scale", 1.0),
+                      kv_e8m0=o.get("kv_e8m0"),
+                      page_indptr=None if case["page_indptr"] is None else case["page_indptr"].cpu().numpy(),
+                      pairs=pairs)
+
+
+def bf16_reference(case, orc, pairs=None):
+    return orc.decode(bits(case["q"]), bits(case["kv"]), case["kv_indptr"].cpu().numpy(),
+                      case["page_table"].cpu().numpy(), case["page_size"],
+                      page_indptr=None if case["page_indptr"] is None else case["page_indptr"].cpu().numpy(),
+                      pairs=pairs)[0]
+
+
+PAIRS = [("bf16", "bf16"), ("bf16", "fp8"), ("fp8", "fp8"), ("bf16", "mxfp4"), ("mxfp4", "mxfp4")]
+SHAPES = [  # (lengths, page_size, num_splits, per_request_pages)
+    ([1, 37, 200], 1, 1, False),
+    ([129, 64, 300, 5], 8, 2, False),
+    ([513, 0, 96], 3, 3, True),
+    ([1000, 31, 257], 16, 7, False),
+    ([40, 33], 8, 64, True),           # more splits than tokens: empty splits
+    ([2048], 8, 1, False),             # one long request, all four waves busy
+]
+
+
+@pytest.mark.parametrize("qf,kf", PAIRS)
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+def test_decode_matches_oracle(orc, qf, kf, shape):
+    lengths, P, S, per_req = SHAPES[shape]
+    print(f"[parity] q={qf} kv={kf} lengths={lengths} P={P} S={S} per_request={per_req}", flush=True)
+    case = synth.make_case(len(lengths), lengths, P, shuffle=True, seed=400 + shape, per_request_pages=per_req,
+                           extra_pages=2)
+    g, o = prepare(case, qf, kf, orc)
+    out = gpu_decode(case, g, S)
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what=f"{qf}/{kf} shape {shape}")
+    # The 0.1/0.1 check against the unquantised cache measures the format's own
+    # error, which the pages judge on benchmark-length sequences.  An mxfp4 row
+    # carries element errors up to a quarter of its block max, and short requests
+    # average over too few rows to stay inside 0.1, so for mxfp4 that check runs
+    # on the full-size 8192-token workloads (test_full_size_workload) only.
+    if kf != "mxfp4":
+        check_close(out, bf16_reference(case, orc), atol=0.1, rtol=0.1, l2=None, what="vs unquantised bf16")
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert not out[b].any()
+
+
+@pytest.mark.parametrize("kf", ["bf16", "fp8", "mxfp4"])
+def test_split_count_invariance(orc, kf):
+    case = synth.make_case(3, [700, 129, 1], 8, shuffle=True, seed=500)
+    g, o = prepare(case, "bf16", kf, orc)
+    ref, _ = oracle_decode(case, o, orc)
+    for S in (1, 2, 3, 8, 32, 256):
+        check_close(gpu_decode(case, g, S), ref, what=f"{kf} S={S}")
+
+
+@pytest.mark.parametrize("kf", ["bf16", "fp8", "mxfp4"])
+def test_one_hot_probe(orc, kf):
+    """A key planted as 16*q (head 0) must dominate head 0: catches gather / paging errors."""
+    case = synth.make_case(2, [300, 77], 8, shuffle=True, seed=600)
+    kv = case["kv"].clone()
+    pt, P = case["page_table"].numpy(), 8
+    plants = ((0, 211), (1, 40))
+    for b, t in plants:
+        gpos = int(case["kv_indptr"][b]) + t
+        row = pt[gpos // P] * P + gpos % P
+        kv[row] = (case["q"][b, 0].float() * 16).to(torch.bfloat16)
+    case["kv"] = kv
+    g, o = prepare(case, "bf16", kf, orc)
+    out = gpu_decode(case, g, 4)
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what=f"one-hot {kf}")
+    for b, t in plants:
+        gpos = int(case["kv_indptr"][b]) + t
+        row = pt[gpos // P] * P + gpos % P
+        vrow = ref[b, 0]
+        assert np.allclose(out[b, 0].cpu().double().numpy(), vrow, atol=0.05 * np.abs(vrow).max())
+
+
+@pytest.mark.parametrize("kf", ["bf16", "fp8", "mxfp4"])
+def test_constant_logits_mean_of_v(orc, kf):
+    case = synth.make_case(2, [100, 333], 4, shuffle=True, seed=700)
+    case["q"] = torch.zeros_like(case["q"])
+    g, o = prepare(case, "bf16", kf, orc)
+    out = gpu_decode(case, g, 3)
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, atol=4e-3, rtol=1e-2, l2=5e-3, what=f"mean-of-V {kf}")
+
+
+def test_deterministic_and_reseeded_buffers(orc):
+    case = synth.make_case(4, [500, 900, 64, 1], 8, shuffle=True, seed=800)
+    g, o = prepare(case, "bf16", "fp8", orc)
+    a = gpu_decode(case, g, 4).clone()
+    b = gpu_decode(case, g, 4).clone()
+    assert torch.equal(a, b)
+    # refill the same device buffers with a different seed: results must follow the new data
+    case2 = synth.make_case(4, [500, 900, 64, 1], 8, shuffle=True, seed=801)
+    g2, o2 = prepare(case2, "bf16", "fp8", orc)
+    g["kv"].copy_(g2["kv"])
+    g["kv_scale"].copy_(g2["kv_scale"])
+    g["q"].copy_(g2["q"])
+    g["page_table"].copy_(g2["page_table"])
+    c = gpu_decode(case, g, 4)
+    ref2, _ = oracle_decode(case2, o2, orc)
+    check_close(c, ref2, what="reseeded")
+
+
+def test_empty_batch_is_noop():
+    q = torch.empty((0, 16, 576), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((8, 576), dtype=torch.bfloat16, device=DEV)
+    ind = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = mla.decode(q, kv, ind, pt, 1, 1)
+    assert out.shape == (0, 16, 512)
+
+
+def test_invalid_arguments_raise():
+    kv = torch.zeros((8, 576), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device=DEV)
+    ind = torch.tensor([0, 8], dtype=torch.int32, device=DEV)
+    pt = torch.zeros(8, dtype=torch.int32, device=DEV)
+    with pytest.raises(mla.StatusError):
+        mla.decode(q, kv, ind, pt, 0, 1)
+    with pytest.raises(mla.StatusError):
+        mla.decode(q, kv, ind, pt, 1, 300)
+    with pytest.raises(mla.StatusError):
+        mla.decode(q.to(torch.float8_e4m3fn), kv, ind, pt, 1, 1)  # fp8 Q with bf16 cache
+
+
+# ------------------------------------------------------- full-size workloads
+def sampled_check(w, orc, n_req=6, seed_offset=0):
+    print(f"[parity-full] {w.name}", flush=True)
+    case = synth.workload_case(w, device=DEV, seed_offset=seed_offset)
+    B, P = w.batch, w.page_size
+    S = w.num_splits or mla.choose_num_splits(B, w.kv_len, {"bf16": 0, "fp8": 1, "mxfp4": 2}[w.kv_fmt])
+    g = {"page_table": case["page_table"], "kv_indptr": case["kv_indptr"], "page_indptr": None}
+    if w.kv_fmt == "fp8":
+        g["kv"], g["kv_scale"] = mla.quantize_fp8(case["kv"])
+    elif w.kv_fmt == "mxfp4":
+        g["kv"], g["kv_scale"] = mla.quantize_mxfp4(case["kv"])
+    else:
+        g["kv"], g["kv_scale"] = case["kv"], None
+    if w.q_fmt == "fp8":
+        g["q"], g["q_scale"] = mla.quantize_fp8(case["q"], w.q_scale)
+    elif w.q_fmt == "mxfp4":
+        p, s = mla.quantize_mxfp4(case["q"].reshape(B * 16, 576))
+        g["q"], g["q_scale"] = p.reshape(B, 16, 288), s
+    else:
+        g["q"], g["q_scale"] = case["q"], None
+    out = gpu_decode(case, g, S).cpu()
+    # the oracle recomputes sampled requests from their own rows, compacted to an identity page table
+    rng = np.random.default_rng(w.index)
+    reqs = sorted(set([0, B - 1] + list(rng.choice(B, size=min(n_req, B), replace=False))))
+    pt = case["page_table"].cpu().numpy()
+    kv_sc = None
+    if w.kv_fmt == "fp8":
+        kv_sc = orc.fp8_scale_from_amax(orc.amax_bf16(bits(case["kv"])))
+        assert float(g["kv_scale"].item()) == kv_sc
+    for b in reqs:
+        L = w.kv_len
+        gpos = b * L + np.arange(L)
+        rows = torch.from_numpy((pt[gpos // P].astype(np.int64) * P + gpos % P))
+        sub_kv = case["kv"][rows.to(DEV)].cpu()
+        sub = {"q": case["q"][b:b + 1].cpu(), "kv": sub_kv, "kv_indptr": torch.tensor([0, L], dtype=torch.int32),
+               "page_table": torch.arange(L, dtype=torch.int32), "page_indptr": None, "page_size": 1}
+        o = {}
+        if w.kv_fmt == "fp8":
+            codes, _ = orc.quant_fp8(bits(sub_kv), kv_sc)
+            assert np.array_equal(codes, u8(g["kv"][rows.to(DEV)]))
+            o.update(kv=codes, kv_dtype="fp8", kv_scale=kv_sc)
+        elif w.kv_fmt == "mxfp4":
+            packed, e8 = orc.quant_mxfp4(bits(sub_kv))
+            assert np.array_equal(packed, u8(g["kv"][rows.to(DEV)]))
+            assert np.array_equal(e8, u8(g["kv_scale"][rows.to(DEV)]))
+            o.update(kv=packed, kv_dtype="mxfp4", kv_e8m0=e8)
+        else:
+            o.update(kv=bits(sub_kv), kv_dtype="bf16")
+        if w.q_fmt == "fp8":
+            codes, qs = orc.quant_fp8(bits(sub["q"]), float(np.float32(w.q_scale)))
+            o.update(q=codes, q_dtype="fp8", q_scale=qs)
+        elif w.q_fmt == "mxfp4":
+            packed, e8 = orc.quant_mxfp4(bits(sub["q"]).reshape(16, 576))
+            o.update(q=packed.reshape(1, 16, 288), q_dtype="mxfp4", q_e8m0=e8)
+        else:
+            o.update(q=bits(sub["q"]), q_dtype="bf16")
+        heads = [0, 5, 15]
+        ref, _ = oracle_decode(sub, o, orc, pairs=[(0, h) for h in heads])
+        for h in heads:
+            check_close(out[b, h], ref[0, h], what=f"{w.name} b={b} h={h}", l2=1e-2)
+        ref16 = bf16_reference(sub, orc, pairs=[(0, h) for h in heads])
+        for h in heads:
+            check_close(out[b, h], ref16[0, h], atol=0.1, rtol=0.1, l2=None, what="vs unquantised bf16")
+    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_full_size_workload(orc, name):
+    sampled_check(synth.WORKLOADS[name], orc)

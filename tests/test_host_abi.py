@@ -1,0 +1,121 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every symbol include/mla_decode.h declares, and its pure-host entry points
+(validation, workspace sizing, split / page-size heuristics, status strings)
+behave as the header documents."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_13_amd as mla
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mla_decode.h")
+
+# fake, 16-byte aligned non-null "device" addresses: validation never dereferences them
+A = 0x10000
+A2 = 0x20000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mla.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    names = declared_functions()
+    assert set(names) == set(mla.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_abi_version(lib):
+    assert lib.mla_abi_version() == 1
+
+
+def v(lib, q=A, qd=mla.BF16, qs=None, kv=A, kd=mla.BF16, ks=None, rows=100, ind=A, batch=4, pt=A,
+      pind=None, P=1, S=1, out=A, ws=None, wsb=0):
+    return lib.mla_validate(q, qd, qs, kv, kd, ks, rows, ind, batch, pt, pind, P, S, out, ws, wsb)
+
+
+def test_validate_ok_and_pairs(lib):
+    assert v(lib) == 0
+    assert v(lib, kd=mla.FP8, ks=A2) == 0
+    assert v(lib, qd=mla.FP8, qs=A2, kd=mla.FP8, ks=A2) == 0
+    assert v(lib, kd=mla.MXFP4, ks=A2) == 0
+    assert v(lib, qd=mla.MXFP4, qs=A2, kd=mla.MXFP4, ks=A2) == 0
+    for qd, kd in ((mla.FP8, mla.BF16), (mla.MXFP4, mla.BF16), (mla.FP8, mla.MXFP4), (mla.MXFP4, mla.FP8),
+                   (mla.BF16, 7), (9, mla.BF16)):
+        assert v(lib, qd=qd, qs=A2, kd=kd, ks=A2) == -2, (qd, kd)
+
+
+def test_validate_errors(lib):
+    assert v(lib, q=None) == -1
+    assert v(lib, out=None) == -1
+    assert v(lib, pt=None) == -1
+    assert v(lib, kd=mla.FP8) == -1            # fp8 cache needs its scale
+    assert v(lib, qd=mla.FP8, kd=mla.FP8, ks=A2) == -1
+    assert v(lib, P=0) == -3
+    assert v(lib, S=0) == -3
+    assert v(lib, S=257) == -3
+    assert v(lib, batch=-1) == -3
+    assert v(lib, rows=0) == -3
+    assert v(lib, q=A + 8) == -4
+    assert v(lib, kv=A + 4) == -4
+    assert v(lib, out=A + 2) == -4
+    assert v(lib, kd=mla.MXFP4, ks=A2 + 4) == -4
+    need = lib.mla_workspace_bytes(4, 8)
+    assert v(lib, S=8) == -5
+    assert v(lib, S=8, ws=A2, wsb=need - 1) == -5
+    assert v(lib, S=8, ws=A2, wsb=need) == 0
+    assert v(lib, S=8, ws=A2 + 8, wsb=need) == -4
+    assert v(lib, batch=0, q=None, out=None) == 0   # empty batch: nothing to do
+
+
+def test_workspace_bytes(lib):
+    assert lib.mla_workspace_bytes(4, 1) == 0
+    assert lib.mla_workspace_bytes(32, 8) == 32 * 8 * 16 * (512 + 1) * 4
+    assert lib.mla_workspace_bytes(0, 8) == 0
+    assert lib.mla_workspace_bytes(4, 0) == 0
+    assert lib.mla_workspace_bytes(4, 257) == 0
+
+
+def test_status_strings(lib):
+    for code in range(-7, 1):
+        assert mla.status_string(code) not in ("", "unknown status")
+    assert mla.status_string(-99) == "unknown status"
+
+
+def test_split_heuristic(lib):
+    for batch in (1, 4, 32, 64, 256, 1000):
+        for L in (1, 31, 1024, 8192, 100000):
+            for kd in (mla.BF16, mla.FP8, mla.MXFP4):
+                s = mla.choose_num_splits(batch, L, kd)
+                assert 1 <= s <= 256
+                assert s == mla.choose_num_splits(batch, L, kd)
+                assert s == 1 or (L + s - 1) // s >= 32  # no split shorter than one sub-tile
+    # a full wave of requests needs no split; small batches split
+    assert mla.choose_num_splits(256, 8192, mla.FP8) == 1
+    assert mla.choose_num_splits(4, 8192, mla.FP8) >= 16
+    assert mla.choose_num_splits(32, 1024, mla.FP8) >= 4
+
+
+def test_page_size_recommendation(lib):
+    assert mla.recommend_page_size(4, 1024) >= 1
+    assert mla.recommend_page_size(256, 8192) >= 1
+
+
+def test_product_path_does_not_touch_the_oracle():
+    root = os.path.join(os.path.dirname(os.path.dirname(__file__)), "mla_latent_kv_13_amd")
+    for dirpath, _, files in os.walk(root):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text and "liboracle" not in text, f
