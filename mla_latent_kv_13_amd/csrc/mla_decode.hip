@@ -138,6 +138,9 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+// Compiler-only fence: LDS reads issued above it cannot be sunk below it, so
+// a batch of fragment reads is in flight together instead of one at a time.
+__device__ __forceinline__ void sched_fence() { asm volatile("" : : : "memory"); }
 
 template <int... I>
 __device__ __forceinline__ void dma_tile(const char* g, uint32_t m0, std::integer_sequence<int, I...>) {
@@ -185,6 +188,25 @@ __device__ __forceinline__ f32x4_t mfma_fp4(i32x4_t a, uint32_t sa, i32x4_t b, u
 }
 
 __device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
+
+// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with
+// gfx950's cross-row swaps: VALU-only, no LDS round trip.
+__device__ __forceinline__ float group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmax3(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax3(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// The softmax reference max is moved only when a logit exceeds it by more
+// than this many binades (base-2 log domain), bounding every weight by 2^8.
+constexpr float kLazy = 8.0f;
 
 // ------------------------------------------------------------- arguments
 struct Stage1Args {
@@ -363,89 +385,164 @@ void stage1_kernel(Stage1Args a) {
   // P*V token slots of this lane group: slot kk <-> token (kk<4 ? 4g+kk : 16+4g+kk-4)
   auto compute = [&](int x, int ntok) {
     const int tb = static_cast<int>(slot_addr(x));
-    // ---------------- QK^T
-    f32x4_t sacc[2];
+    // fp8 V^T fragments for P*V, one transposing read per 16-column tile:
+    // lane j of a 16-lane group addresses token T[j/2] (8 B at column 8*(j%2)),
+    // T = {4g..4g+3, 16+4g..16+4g+3}; lane i then holds column i of all eight.
+    i32x2_t vv[KF == FFP8 ? 32 : 1];
+    const int tvj = (lane & 15) >> 1;
+    const int tv8 = tvj < 4 ? 4 * g + tvj : 16 + 4 * g + (tvj - 4);
+    const int vbe = tb + 16 * swz(tv8) + 8 * (lane & 1);
+    const int vbo = tb + 512 + 16 * (swz(tv8) ^ 4) + 8 * (lane & 1);
+    auto tr8_frag = [&](int c) {
+      return __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<__attribute__((address_space(3))) i32x2_t*>(
+          static_cast<uintptr_t>((c & 1 ? vbo : vbe) + 1024 * (c >> 1))));
+    };
+    // ---------------- QK^T: both 16-token tiles at once (two independent
+    // accumulator chains), every LDS fragment fetched before the MFMAs run.
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    const int ko0 = 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(tq0) ^ ((g & 1) << 2));
+    const int ko1 = 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(tq1) ^ ((g & 1) << 2));
+    if constexpr (KF == FBF16) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int t = h2 ? tq1 : tq0;
-      f32x4_t sa = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (KF == FBF16) {
-        const int base = tb + 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(t) ^ ((g & 1) << 2));
+      for (int hh2 = 0; hh2 < 2; ++hh2) {
+        bf16x8_t k0[9], k1[9];
 #pragma unroll
-        for (int m = 0; m < 18; ++m) sa = mfma_bf16(lds_ld<bf16x8_t>(base + 2048 * m), qb[m], sa);
-      } else if constexpr (KF == FFP8 && QF == FBF16) {
-        const int base = tb + 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(t) ^ ((g & 1) << 2));
-#pragma unroll
-        for (int c = 0; c < 9; ++c) {
-          const i32x4_t u = lds_ld<i32x4_t>(base + 2048 * c);
-          sa = mfma_bf16(cvt_fp8x8(i32x2_t{u.x, u.y}), qb[2 * c], sa);
-          sa = mfma_bf16(cvt_fp8x8(i32x2_t{u.z, u.w}), qb[2 * c + 1], sa);
+        for (int i = 0; i < 9; ++i) {
+          k0[i] = lds_ld<bf16x8_t>(tb + ko0 + 2048 * (9 * hh2 + i));
+          k1[i] = lds_ld<bf16x8_t>(tb + ko1 + 2048 * (9 * hh2 + i));
         }
-      } else if constexpr (KF == FFP8) {  // fp8 x fp8
-        const int be = tb + 1024 * g + 16 * swz(t);
-        const int bo = tb + 1024 * g + 512 + 16 * (swz(t) ^ 4);
+        sched_fence();
 #pragma unroll
-        for (int c = 0; c < 5; ++c) {
-          i32x8_t av = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (c < 4 || g < 2) {
-            const i32x4_t u0 = lds_ld<i32x4_t>(be + 4096 * c);
-            const i32x4_t u1 = lds_ld<i32x4_t>(bo + 4096 * c);
-            av = i32x8_t{u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-          }
-          sa = mfma_fp8(av, q8[c], sa);
-        }
-      } else {  // mxfp4 K
-        const int sbase = static_cast<int>(sc_addr(x)) + 20 * t + 2 * lds_ld<uint8_t>(static_cast<int>(par_addr(x)) + t);
-        const int base = tb + 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(t) ^ ((g & 1) << 2));
-        if constexpr (QF == FBF16) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const i32x4_t u = lds_ld<i32x4_t>(base + 2048 * c);
-            const float sc = e8m0_f32(lds_ld<uint8_t>(sbase + 4 * c + g));
-            sa = mfma_bf16(cvt_fp4x8(u.x, sc), qb[4 * c + 0], sa);
-            sa = mfma_bf16(cvt_fp4x8(u.y, sc), qb[4 * c + 1], sa);
-            sa = mfma_bf16(cvt_fp4x8(u.z, sc), qb[4 * c + 2], sa);
-            sa = mfma_bf16(cvt_fp4x8(u.w, sc), qb[4 * c + 3], sa);
-          }
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const uint32_t u = lds_ld<uint32_t>(tb + 8192 + 512 * e + 16 * (swz(t) ^ (e << 2)) + 4 * g);
-            const float sc = e8m0_f32(lds_ld<uint8_t>(sbase + 16 + e));
-            sa = mfma_bf16(cvt_fp4x8(u, sc), qb[16 + e], sa);
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const i32x4_t u = lds_ld<i32x4_t>(base + 2048 * c);
-            const uint32_t sc = lds_ld<uint8_t>(sbase + 4 * c + g);
-            sa = mfma_fp4(u, sc, q4[c], q4s[c], sa);
-          }
-          i32x4_t ur = {0, 0, 0, 0};
-          uint32_t scr = 127u;
-          if (g < 2) {
-            ur = lds_ld<i32x4_t>(tb + 8192 + 512 * g + 16 * (swz(t) ^ (g << 2)));
-            scr = lds_ld<uint8_t>(sbase + 16 + g);
-          }
-          sa = mfma_fp4(ur, scr, q4[4], q4s[4], sa);
+        for (int i = 0; i < 9; ++i) {
+          s0 = mfma_bf16(k0[i], qb[9 * hh2 + i], s0);
+          s1 = mfma_bf16(k1[i], qb[9 * hh2 + i], s1);
         }
       }
-      sacc[h2] = sa;
+    } else if constexpr (KF == FFP8 && QF == FBF16) {
+      i32x4_t k0[9], k1[9];
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        k0[c] = lds_ld<i32x4_t>(tb + ko0 + 2048 * c);
+        k1[c] = lds_ld<i32x4_t>(tb + ko1 + 2048 * c);
+      }
+      // the P*V fragments do not depend on the softmax: fetch them now too
+#pragma unroll
+      for (int c = 0; c < 32; ++c) vv[c] = tr8_frag(c);
+      sched_fence();
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        s0 = mfma_bf16(cvt_fp8x8(i32x2_t{k0[c].x, k0[c].y}), qb[2 * c], s0);
+        s1 = mfma_bf16(cvt_fp8x8(i32x2_t{k1[c].x, k1[c].y}), qb[2 * c], s1);
+        s0 = mfma_bf16(cvt_fp8x8(i32x2_t{k0[c].z, k0[c].w}), qb[2 * c + 1], s0);
+        s1 = mfma_bf16(cvt_fp8x8(i32x2_t{k1[c].z, k1[c].w}), qb[2 * c + 1], s1);
+      }
+    } else if constexpr (KF == FFP8) {  // fp8 x fp8
+      const int e0 = tb + 1024 * g + 16 * swz(tq0), o0 = tb + 1024 * g + 512 + 16 * (swz(tq0) ^ 4);
+      const int e1 = tb + 1024 * g + 16 * swz(tq1), o1 = tb + 1024 * g + 512 + 16 * (swz(tq1) ^ 4);
+      i32x8_t a0[5], a1[5];
+#pragma unroll
+      for (int c = 0; c < 5; ++c) {
+        a0[c] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        a1[c] = a0[c];
+        if (c < 4 || g < 2) {
+          const i32x4_t u0 = lds_ld<i32x4_t>(e0 + 4096 * c), u1 = lds_ld<i32x4_t>(o0 + 4096 * c);
+          const i32x4_t w0 = lds_ld<i32x4_t>(e1 + 4096 * c), w1 = lds_ld<i32x4_t>(o1 + 4096 * c);
+          a0[c] = i32x8_t{u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+          a1[c] = i32x8_t{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 32; ++c) vv[c] = tr8_frag(c);
+      sched_fence();
+#pragma unroll
+      for (int c = 0; c < 5; ++c) {
+        s0 = mfma_fp8(a0[c], q8[c], s0);
+        s1 = mfma_fp8(a1[c], q8[c], s1);
+      }
+    } else {  // mxfp4 K: block scales read once per (token, block)
+      const int pr = static_cast<int>(par_addr(x));
+      const int sb0 = static_cast<int>(sc_addr(x)) + 20 * tq0 + 2 * lds_ld<uint8_t>(pr + tq0);
+      const int sb1 = static_cast<int>(sc_addr(x)) + 20 * tq1 + 2 * lds_ld<uint8_t>(pr + tq1);
+      if constexpr (QF == FBF16) {
+        i32x4_t u0[4], u1[4];
+        uint32_t r0[2], r1[2], c0[6], c1[6];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u0[c] = lds_ld<i32x4_t>(tb + ko0 + 2048 * c);
+          u1[c] = lds_ld<i32x4_t>(tb + ko1 + 2048 * c);
+          c0[c] = lds_ld<uint8_t>(sb0 + 4 * c + g);
+          c1[c] = lds_ld<uint8_t>(sb1 + 4 * c + g);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          r0[e] = lds_ld<uint32_t>(tb + 8192 + 512 * e + 16 * (swz(tq0) ^ (e << 2)) + 4 * g);
+          r1[e] = lds_ld<uint32_t>(tb + 8192 + 512 * e + 16 * (swz(tq1) ^ (e << 2)) + 4 * g);
+          c0[4 + e] = lds_ld<uint8_t>(sb0 + 16 + e);
+          c1[4 + e] = lds_ld<uint8_t>(sb1 + 16 + e);
+        }
+        sched_fence();
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float f0 = e8m0_f32(c0[c]), f1 = e8m0_f32(c1[c]);
+          s0 = mfma_bf16(cvt_fp4x8(u0[c].x, f0), qb[4 * c + 0], s0);
+          s1 = mfma_bf16(cvt_fp4x8(u1[c].x, f1), qb[4 * c + 0], s1);
+          s0 = mfma_bf16(cvt_fp4x8(u0[c].y, f0), qb[4 * c + 1], s0);
+          s1 = mfma_bf16(cvt_fp4x8(u1[c].y, f1), qb[4 * c + 1], s1);
+          s0 = mfma_bf16(cvt_fp4x8(u0[c].z, f0), qb[4 * c + 2], s0);
+          s1 = mfma_bf16(cvt_fp4x8(u1[c].z, f1), qb[4 * c + 2], s1);
+          s0 = mfma_bf16(cvt_fp4x8(u0[c].w, f0), qb[4 * c + 3], s0);
+          s1 = mfma_bf16(cvt_fp4x8(u1[c].w, f1), qb[4 * c + 3], s1);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          s0 = mfma_bf16(cvt_fp4x8(r0[e], e8m0_f32(c0[4 + e])), qb[16 + e], s0);
+          s1 = mfma_bf16(cvt_fp4x8(r1[e], e8m0_f32(c1[4 + e])), qb[16 + e], s1);
+        }
+      } else {
+        i32x4_t u0[5], u1[5];
+        uint32_t c0[5], c1[5];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u0[c] = lds_ld<i32x4_t>(tb + ko0 + 2048 * c);
+          u1[c] = lds_ld<i32x4_t>(tb + ko1 + 2048 * c);
+          c0[c] = lds_ld<uint8_t>(sb0 + 4 * c + g);
+          c1[c] = lds_ld<uint8_t>(sb1 + 4 * c + g);
+        }
+        u0[4] = i32x4_t{0, 0, 0, 0};
+        u1[4] = u0[4];
+        c0[4] = 127u;
+        c1[4] = 127u;
+        if (g < 2) {
+          u0[4] = lds_ld<i32x4_t>(tb + 8192 + 512 * g + 16 * (swz(tq0) ^ (g << 2)));
+          u1[4] = lds_ld<i32x4_t>(tb + 8192 + 512 * g + 16 * (swz(tq1) ^ (g << 2)));
+          c0[4] = lds_ld<uint8_t>(sb0 + 16 + g);
+          c1[4] = lds_ld<uint8_t>(sb1 + 16 + g);
+        }
+        sched_fence();
+#pragma unroll
+        for (int c = 0; c < 5; ++c) {
+          s0 = mfma_fp4(u0[c], c0[c], q4[c], q4s[c], s0);
+          s1 = mfma_fp4(u1[c], c1[c], q4[c], q4s[c], s1);
+        }
+      }
     }
     // ---------------- online softmax (log2 domain); lane holds head hq,
-    // tokens 4g+r (tile 0) and 16+4g+r (tile 1)
+    // tokens 4g+r (tile 0) and 16+4g+r (tile 1).  The reference max is only
+    // moved when a logit exceeds it by more than 2^kLazy, so the O rescale
+    // (all 128 accumulators) runs a handful of times per request; the
+    // weights stay <= 2^kLazy and the final division uses the same reference.
     float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = (4 * g + r < ntok) ? sacc[0][r] * c_log2 : -__builtin_huge_valf();
-      sv[4 + r] = (16 + 4 * g + r < ntok) ? sacc[1][r] * c_log2 : -__builtin_huge_valf();
+      sv[r] = (4 * g + r < ntok) ? s0[r] * c_log2 : -__builtin_huge_valf();
+      sv[4 + r] = (16 + 4 * g + r < ntok) ? s1[r] * c_log2 : -__builtin_huge_valf();
     }
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmax3(mx, sv[i]);
-    mx = fmax3(mx, __shfl_xor(mx, 16));
-    mx = fmax3(mx, __shfl_xor(mx, 32));
-    const float m_new = fmax3(m_run, mx);
-    if (__any(m_new > m_run)) {
+    mx = group_max(mx);
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmax3(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -471,26 +568,25 @@ void stage1_kernel(Stage1Args a) {
       const int ba = tb + 512 * kb + 16 * (swz(ta) ^ (kb << 2)) + 8 * (j & 1);
       const int bc = tb + 512 * kb + 16 * (swz(tc) ^ (kb << 2)) + 8 * (j & 1);
 #pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(static_cast<uintptr_t>(ba + 1024 * c)));
-        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(static_cast<uintptr_t>(bc + 1024 * c)));
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[c] = mfma_bf16(av, pb, acc[c]);
+      for (int cg = 0; cg < 4; ++cg) {
+        i16x4_t v0[8], v1[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v0[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(static_cast<uintptr_t>(ba + 1024 * (8 * cg + e))));
+          v1[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(static_cast<uintptr_t>(bc + 1024 * (8 * cg + e))));
+        }
+        sched_fence();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0[e], v1[e], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[8 * cg + e] = mfma_bf16(av, pb, acc[8 * cg + e]);
+        }
       }
     } else if constexpr (KF == FFP8) {
-      const int j = lane & 15;
-      const int kk = j >> 1;
-      const int tv = kk < 4 ? 4 * g + kk : 16 + 4 * g + (kk - 4);
-      const int be = tb + 16 * swz(tv) + 8 * (j & 1);
-      const int bo = tb + 512 + 16 * (swz(tv) ^ 4) + 8 * (j & 1);
 #pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<__attribute__((address_space(3))) i32x2_t*>(
-            static_cast<uintptr_t>((c & 1 ? bo : be) + 1024 * (c >> 1))));
-        acc[c] = mfma_bf16(cvt_fp8x8(v), pb, acc[c]);
-      }
+      for (int c = 0; c < 32; ++c) acc[c] = mfma_bf16(cvt_fp8x8(vv[c]), pb, acc[c]);
     } else {
       // mxfp4: lane (column block i = lane&15) decodes unit i of its 8 tokens;
       // output tile c row r <-> latent column 32*(4g+r) + c.
@@ -509,6 +605,7 @@ void stage1_kernel(Stage1Args a) {
         vw[kk][3] = u.w;
         vsc[kk] = e8m0_f32(lds_ld<uint8_t>(sc0 + 20 * tv + 2 * lds_ld<uint8_t>(pr0 + tv) + i));
       }
+      sched_fence();
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         uint32_t cv[8][4];  // token kk: bf16 pairs (cols 8qd + 2e, +1)
@@ -569,8 +666,7 @@ void stage1_kernel(Stage1Args a) {
   }
 
   // ---- merge the four waves (log2-domain weights), then write
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = group_sum(l_run);
   __syncthreads();
   const int ob0 = static_cast<int>(smem0);
   const int mlb = ob0 + 2 * 128 * 64 * 4;  // m[w][16], l[w][16]
