@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=list(synth.WORKLOADS))
     ap.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of decoding, run a plain device-to-device copy of this many bytes "
+                         "(the known-size reference used to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -177,6 +180,20 @@ def main():
         sys.exit(2)
     mla.load()
     device = "cuda"
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"metric": "device copy", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                          "us_per_copy": round(dt * 1e6, 2), "gbs": round(2 * src.numel() * 4 / dt / 1e9, 1)}))
+        return
     w = synth.WORKLOADS[args.workload]
     print(f"[bench] headline {w.name}", file=sys.stderr, flush=True)
     head, wall = time_workload(w, args.steps, args.warmup, device)

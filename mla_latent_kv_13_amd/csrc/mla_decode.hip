@@ -273,56 +273,6 @@ void stage1_kernel(Stage1Args a) {
   const int32_t* ptab = a.page_table + (a.page_indptr ? a.page_indptr[b] : 0);
   const uint32_t P = static_cast<uint32_t>(a.page_size);
 
-  // ---- Q fragments (B operands) for this lane's head
-  constexpr int NQ = QFrag<QF, KF>::kN;
-  bf16x8_t qb[QF == FBF16 ? NQ : 1];
-  i32x8_t q8[QF == FFP8 ? NQ : 1];
-  i32x4_t q4[QF == FMX ? NQ : 1];
-  uint32_t q4s[QF == FMX ? NQ : 1];
-  float qs = 1.0f, ks = 1.0f;
-  if constexpr (QF == FBF16) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qrow + qdim_bf16<KF>(m, g));
-  } else if constexpr (QF == FFP8) {
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) q8[c] = *reinterpret_cast<const i32x8_t*>(qrow + 128 * c + 32 * g);
-    q8[4] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    if (g < 2) q8[4] = *reinterpret_cast<const i32x8_t*>(qrow + 512 + 32 * g);
-    qs = *static_cast<const float*>(a.q_scale);
-  } else {
-    const size_t qr = static_cast<size_t>(b) * kHeads + hq;
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * MLA_MXFP4_ROW_BYTES;
-    const uint8_t* qsc = static_cast<const uint8_t*>(a.q_scale) + qr * MLA_MXFP4_ROW_SCALES;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      q4[c] = *reinterpret_cast<const i32x4_t*>(qrow + 64 * c + 16 * g);
-      q4s[c] = qsc[4 * c + g];
-    }
-    q4[4] = i32x4_t{0, 0, 0, 0};
-    q4s[4] = 127u;
-    if (g < 2) {
-      q4[4] = *reinterpret_cast<const i32x4_t*>(qrow + 256 + 16 * g);
-      q4s[4] = qsc[16 + g];
-    }
-  }
-  if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
-  const float c_log2 = a.sm_scale_log2e * qs * ks;
-  const float out_mul = KF == FFP8 ? ks : 1.0f;
-  // Make the Q loads complete before the asynchronous stream starts, so the
-  // compiler's own wait for them cannot drain the in-flight tiles later.
-  if constexpr (QF == FBF16) {
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(qb[m]));
-  } else if constexpr (QF == FFP8) {
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q8[m]));
-  } else {
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q4[m]), "+v"(q4s[m]));
-  }
-
   // ---- per-wave LDS ring
   const uint32_t wbase = smem0 + static_cast<uint32_t>(w) * L::kWaveBytes;
   auto slot_addr = [&](int x) { return wbase + static_cast<uint32_t>(x) * L::kSlot; };
@@ -372,6 +322,64 @@ void stage1_kernel(Stage1Args a) {
       dma_tile(gp, slot_addr(x), std::make_integer_sequence<int, Kv<KF>::kNdmaX4>{});
     }
   };
+
+  // The first page-id gathers go out before the Q loads so that both
+  // latencies overlap; one wait then covers them.
+  if (nloc > 0) {
+#pragma unroll
+    for (int X = 0; X < D; ++X) issue_pid(X);
+  }
+
+  // ---- Q fragments (B operands) for this lane's head
+  constexpr int NQ = QFrag<QF, KF>::kN;
+  bf16x8_t qb[QF == FBF16 ? NQ : 1];
+  i32x8_t q8[QF == FFP8 ? NQ : 1];
+  i32x4_t q4[QF == FMX ? NQ : 1];
+  uint32_t q4s[QF == FMX ? NQ : 1];
+  float qs = 1.0f, ks = 1.0f;
+  if constexpr (QF == FBF16) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qrow + qdim_bf16<KF>(m, g));
+  } else if constexpr (QF == FFP8) {
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q8[c] = *reinterpret_cast<const i32x8_t*>(qrow + 128 * c + 32 * g);
+    q8[4] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (g < 2) q8[4] = *reinterpret_cast<const i32x8_t*>(qrow + 512 + 32 * g);
+    qs = *static_cast<const float*>(a.q_scale);
+  } else {
+    const size_t qr = static_cast<size_t>(b) * kHeads + hq;
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * MLA_MXFP4_ROW_BYTES;
+    const uint8_t* qsc = static_cast<const uint8_t*>(a.q_scale) + qr * MLA_MXFP4_ROW_SCALES;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      q4[c] = *reinterpret_cast<const i32x4_t*>(qrow + 64 * c + 16 * g);
+      q4s[c] = qsc[4 * c + g];
+    }
+    q4[4] = i32x4_t{0, 0, 0, 0};
+    q4s[4] = 127u;
+    if (g < 2) {
+      q4[4] = *reinterpret_cast<const i32x4_t*>(qrow + 256 + 16 * g);
+      q4s[4] = qsc[16 + g];
+    }
+  }
+  if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
+  const float c_log2 = a.sm_scale_log2e * qs * ks;
+  const float out_mul = KF == FFP8 ? ks : 1.0f;
+  // Wait for the page ids and Q together, and make the compiler see Q as
+  // complete here, so its own wait for Q cannot drain the in-flight tiles later.
+  wait_vm<0>();
+  if constexpr (QF == FBF16) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(qb[m]));
+  } else if constexpr (QF == FFP8) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q8[m]));
+  } else {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q4[m]), "+v"(q4s[m]));
+  }
 
   // ---- running softmax state (head hq) and the O^T accumulators
   f32x4_t acc[32];
@@ -633,9 +641,6 @@ void stage1_kernel(Stage1Args a) {
 
   // ---- the asynchronous pipeline
   if (nloc > 0) {
-#pragma unroll
-    for (int X = 0; X < D; ++X) issue_pid(X);
-    wait_vm<0>();
     const int nfill = min(NBUF, nloc);
     for (int X = 0; X < nfill; ++X) {
       if (X >= D) wait_vm<D * NDMA + D - 1>();
@@ -749,18 +754,47 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
   const int hq = ((blockIdx.x & 3) << 2) + (threadIdx.x >> 6);
   const int col = 8 * (threadIdx.x & 63);
   const float* lse = part_lse + static_cast<size_t>(b) * S * kHeads + hq;
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < S; ++s) M = fmax3(M, lse[s * kHeads]);
+  const float* po = part_o + (static_cast<size_t>(b) * S * kHeads + hq) * kDv + col;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  // pass 1: the largest split LSE, eight independent loads in flight per step
+  float M = kNegInf;
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = lse[(s + i) * kHeads];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) M = fmax3(M, v[i]);
+  }
+  for (; s < S; ++s) M = fmax3(M, lse[s * kHeads]);
+  // pass 2: weighted sum, four splits (eight 16-byte loads) in flight per step;
+  // an empty split (LSE = -inf) gets weight 0
   f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   float ws = 0.0f;
-  if (M != -__builtin_huge_valf()) {
-    for (int s = 0; s < S; ++s) {
+  if (M != kNegInf) {
+    s = 0;
+    for (; s + 4 <= S; s += 4) {
+      float l[4];
+      f32x4_t x0[4], x1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        l[i] = lse[(s + i) * kHeads];
+        x0[i] = *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(s + i) * kHeads * kDv);
+        x1[i] = *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(s + i) * kHeads * kDv + 4);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float wgt = l[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l[i] - M);
+        a0 += x0[i] * wgt;
+        a1 += x1[i] * wgt;
+        ws += wgt;
+      }
+    }
+    for (; s < S; ++s) {
       const float l = lse[s * kHeads];
-      if (l == -__builtin_huge_valf()) continue;
-      const float wgt = __builtin_amdgcn_exp2f(l - M);
-      const float* po = part_o + ((static_cast<size_t>(b) * S + s) * kHeads + hq) * kDv + col;
-      a0 += *reinterpret_cast<const f32x4_t*>(po) * wgt;
-      a1 += *reinterpret_cast<const f32x4_t*>(po + 4) * wgt;
+      const float wgt = l == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l - M);
+      a0 += *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(s) * kHeads * kDv) * wgt;
+      a1 += *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(s) * kHeads * kDv + 4) * wgt;
       ws += wgt;
     }
   }
