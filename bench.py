@@ -87,24 +87,39 @@ def time_workload(w, steps, warmup, device):
         mla.decode(r["q"], r["kv"], r["kv_indptr"], r["page_table"], w.page_size, S, q_scale=r["q_scale"],
                    kv_scale=r["kv_scale"], out=r["out"], workspace=r["ws"])
 
-    for i in range(warmup):
+    # warm up for at least `warmup` calls and ~0.3 s, so clocks and caches settle
+    i = 0
+    t_end = time.perf_counter() + 0.3
+    while i < warmup or time.perf_counter() < t_end:
         call(i)
+        i += 1
+        if i % 32 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # `steps` timed calls, in five back-to-back groups timed with HIP events on
+    # the launch stream; the headline is the median group (per call)
+    ngroups = 5
+    per = max(1, steps // ngroups)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ngroups)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
-        call(warmup + i)
-    e1.record(stream)
+    k = i
+    for r in range(ngroups):
+        evs[r][0].record(stream)
+        for _ in range(per):
+            call(k)
+            k += 1
+        evs[r][1].record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    ev_ms = e0.elapsed_time(e1) / steps
+    wall = (time.perf_counter() - t0) / (ngroups * per)
+    group_ms = sorted(e0.elapsed_time(e1) / per for e0, e1 in evs)
+    ev_ms = group_ms[len(group_ms) // 2]
     nbytes = compulsory_bytes(w, w.page_size)
     res = {
         "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q": w.q_fmt, "kv": w.kv_fmt,
         "page_size": w.page_size, "num_splits": S, "replicas": nrep,
-        "us_per_call": round(ev_ms * 1e3, 3), "wall_us_per_call": round(wall * 1e6, 3),
+        "us_per_call": round(ev_ms * 1e3, 3), "us_min": round(group_ms[0] * 1e3, 3),
+        "us_max": round(group_ms[-1] * 1e3, 3), "wall_us_per_call": round(wall * 1e6, 3),
         "compulsory_bytes": nbytes, "gbs": round(nbytes / (ev_ms * 1e-3) / 1e9, 1),
         "frac_of_peak": round(nbytes / (ev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "partial_bytes": 2 * ws_bytes,

@@ -95,20 +95,28 @@ template <int KF> struct Lay {
   static constexpr int kScOff = kNbuf * kSlot;
   static constexpr int kParOff = kScOff + kNbuf * kScSlot;
   static constexpr int kPidOff = kParOff + kNbuf * kParSlot;
-  static constexpr int kWaveBytes = kPidOff + kNpid * kPidSlot;
+  static constexpr int kRowOff = kPidOff + kNpid * kPidSlot;       // physical row per token (u32)
+  static constexpr int kPtrOff = kRowOff + 4 * kSub;                // row base address per token (u64)
+  static constexpr int kWaveBytes = kPtrOff + 8 * kSub;
   static constexpr int kCombine = 2 * 128 * 64 * 4 + 2 * kWaves * kHeads * 4;
   static constexpr int kTotal = kWaves * kWaveBytes > kCombine ? kWaves * kWaveBytes : kCombine;
   static constexpr int kNdma = Kv<KF>::kNdmaX4 + Kv<KF>::kNdmaSc;  // VMEM instrs per sub-tile
 };
 
-// Byte offset, inside a slot, of 16-byte unit k of sub-tile token t (0..31).
-// Units are stored [k/2][k%2][slot]: one DMA instruction fills units 2i, 2i+1
-// of all 32 tokens.  The slot index is swizzled so that the QK reads (8 rows
-// of one unit), the transposing P*V reads (8 tokens of one unit) and the bf16
-// pairs of units all land on distinct banks.
-__device__ __forceinline__ int swz(int t) { return t ^ ((t >> 2) & 4); }
-__device__ __forceinline__ int unit_off(int t, int k) {
-  return 1024 * (k >> 1) + 512 * (k & 1) + 16 * (swz(t) ^ ((k & 1) << 2));
+// A sub-tile is stored as its row-major byte stream: token t's 16-byte unit k
+// sits in LDS chunk t*U + (k ^ tswz(t)).  The swizzle only flips the two low
+// bits of the unit index with bits of the token index; U is a multiple of 4
+// for bf16/fp8, so the map stays inside each token's row and is an
+// involution, and the DMA instruction that fills chunks 64i..64i+63 still
+// reads 1 KB of consecutive stream bytes.  The token bits were chosen by an
+// exhaustive search over a 64-bank model so that the QK fragment reads
+// (8 tokens, one unit), the transposing P*V reads and the mxfp4 block reads
+// all hit distinct banks; mxfp4 needs no swizzle (U = 18).
+template <int KF>
+__device__ __forceinline__ int tswz(int t) {
+  if constexpr (KF == FFP8) return (((t >> 2) ^ (t >> 4)) & 1) << 1;
+  else if constexpr (KF == FBF16) return ((t >> 2) & 1) | (((t >> 1) & 1) << 1);
+  else return 0;
 }
 
 // ------------------------------------------------------------- primitives
@@ -121,17 +129,20 @@ __device__ __forceinline__ void lds_st(int off, T v) {
   *reinterpret_cast<__attribute__((address_space(3))) T*>(static_cast<uintptr_t>(off)) = v;
 }
 
-// Direct-to-LDS loads.  LDS address = m0 + offset + 16*lane (x4) or 4*lane (dword);
-// the immediate offset is added to the global address as well.
-template <int OFF>
-__device__ __forceinline__ void dma_x4(const void* g, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+// Direct-to-LDS loads.  LDS address = m0 + 16*lane (x4) or m0 + 4*lane (dword).
+// Cache rows are read exactly once, so the 16-byte stream loads carry the
+// non-temporal policy bit.
+__device__ __forceinline__ void dma_x4_nt(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
-               : "v"(g), "s"(m0), "n"(OFF)
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(m0))
                : "memory");
 }
 __device__ __forceinline__ void dma_b32(const void* g, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(m0) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(m0))
+               : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -141,11 +152,20 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 // Compiler-only fence: LDS reads issued above it cannot be sunk below it, so
 // a batch of fragment reads is in flight together instead of one at a time.
 __device__ __forceinline__ void sched_fence() { asm volatile("" : : : "memory"); }
-
-template <int... I>
-__device__ __forceinline__ void dma_tile(const char* g, uint32_t m0, std::integer_sequence<int, I...>) {
-  (dma_x4<32 * I>(g, m0 + 992u * I), ...);
+// Pin eight fragments: their loads must have completed here (the compiler
+// waits for exactly these), later reads stay below and in flight, and the
+// consumers of the values cannot be hoisted above.
+template <class T>
+__device__ __forceinline__ void pin2(T& a, T& b) {
+  asm volatile("" : "+v"(a), "+v"(b) : : "memory");
 }
+template <class T>
+__device__ __forceinline__ void pin8(T* v) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+               :
+               : "memory");
+}
+
 
 __device__ __forceinline__ float e8m0_f32(uint32_t e) {
   return __uint_as_float(e ? (e << 23) : 0x00400000u);
@@ -280,9 +300,6 @@ void stage1_kernel(Stage1Args a) {
   auto par_addr = [&](int x) { return wbase + L::kParOff + static_cast<uint32_t>(x) * L::kParSlot; };
   auto pid_addr = [&](int y) { return wbase + L::kPidOff + static_cast<uint32_t>(y % L::kNpid) * L::kPidSlot; };
 
-  // DMA lane role: lane fills units 2i + hh of token tdma in every instruction i.
-  const int hh = lane >> 5;
-  const int tdma = swz((lane & 31) ^ (hh << 2));
 
   auto issue_pid = [&](int X) {
     const int xc = X < nloc ? X : (nloc > 0 ? nloc - 1 : 0);
@@ -290,36 +307,77 @@ void stage1_kernel(Stage1Args a) {
     const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
     dma_b32(ptab + gpos / P, pid_addr(X));
   };
-  auto row_of = [&](int X, int t) -> int64_t {  // physical row of sub-tile X, token t (page id already staged)
-    const int tok = min(kSub * (w + kWaves * X) + t, n - 1);
-    const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
-    const int pid = lds_ld<int>(static_cast<int>(pid_addr(X)) + 4 * t);
-    return static_cast<int64_t>(pid) * P + gpos % P;
+  constexpr int U = Kv<KF>::kUnits;
+  // Per DMA instruction i, this lane fills LDS chunk 64i + lane = token t,
+  // stored unit k (stream unit k ^ tswz(t)), packed as (8t << 16) | 16*(stream
+  // unit): the row-pointer table offset and the byte offset inside the row.
+  // Formats with up to 18 instructions per sub-tile keep these in registers;
+  // bf16 (36) recomputes them from an opaque lane index instead.
+  constexpr bool kPre = Kv<KF>::kNdmaX4 <= 18;
+  auto dma_pack = [](int i, int ln) {
+    const int c = 64 * i + ln;
+    const int t = c / U;
+    return ((8 * t) << 16) | (16 * ((c - t * U) ^ tswz<KF>(t)));
   };
+  int dmao[kPre ? Kv<KF>::kNdmaX4 : 1];
+#pragma unroll
+  for (int i = 0; i < (kPre ? Kv<KF>::kNdmaX4 : 1); ++i) dmao[i] = dma_pack(i, lane);
   auto issue_tile = [&](int X) {
     const int x = X % NBUF;
-    const int64_t row = row_of(X, tdma);
-    const char* gp = a.kv + row * ROW + 16 * hh;
+    wait_lgkm0();  // every LDS read of the slot being refilled has completed
+    const int ub = kSub * (w + kWaves * X);
+    const int nv = min(kSub, n - ub);
+    const int rt = static_cast<int>(wbase + L::kRowOff);
+    const int pt = static_cast<int>(wbase + L::kPtrOff);
+    // physical row (and its base address) of each of the 32 tokens; tokens
+    // past the end repeat the last valid one, so a tail sub-tile stays finite
+    // and in bounds
+    if (lane < kSub) {
+      const int tok = ub + min(lane, nv - 1);
+      const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
+      const uint32_t pid = static_cast<uint32_t>(lds_ld<int>(static_cast<int>(pid_addr(X)) + 4 * lane));
+      const uint32_t row = pid * P + gpos % P;
+      lds_st<uint32_t>(rt + 4 * lane, row);
+      lds_st<uint64_t>(pt + 8 * lane, reinterpret_cast<uint64_t>(a.kv + static_cast<int64_t>(row) * ROW));
+      if constexpr (KF == FMX) lds_st<uint8_t>(static_cast<int>(par_addr(x)) + lane, static_cast<uint8_t>(row & 1));
+    }
+    // Row-pointer reads in batches of up to 18 (one LDS latency per batch),
+    // each batch followed by its DMA instructions.
+    constexpr int NB = Kv<KF>::kNdmaX4 < 18 ? Kv<KF>::kNdmaX4 : 18;
+    int lnv = lane;
+    if constexpr (!kPre) asm volatile("" : "+v"(lnv));
+    auto issue_x4 = [&](int x) {
+#pragma unroll
+      for (int i0 = 0; i0 < Kv<KF>::kNdmaX4; i0 += NB) {
+        uint64_t rptr[NB];
+        int off[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          if constexpr (kPre) off[i] = dmao[i0 + i];
+          else off[i] = dma_pack(i0 + i, lnv);
+          rptr[i] = lds_ld<uint64_t>(pt + (off[i] >> 16));
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          dma_x4_nt(reinterpret_cast<const char*>(rptr[i]) + (off[i] & 0xffff), slot_addr(x) + 1024u * (i0 + i));
+      }
+    };
     if constexpr (KF == FMX) {
       const uint8_t* ksc = static_cast<const uint8_t*>(a.kv_scale);
-      int64_t srow[3];
-      int sw[3];
+      const uint8_t* sp[3];
 #pragma unroll
       for (int i2 = 0; i2 < 3; ++i2) {
         const int d = 64 * i2 + lane;
         const int td = d < 160 ? d / 5 : 0;
-        sw[i2] = d < 160 ? d - 5 * td : 0;
-        srow[i2] = row_of(X, td);
+        const int sw = d < 160 ? d - 5 * td : 0;
+        const int64_t srow = lds_ld<uint32_t>(rt + 4 * td);
+        sp[i2] = ksc + ((18 * srow) & ~static_cast<int64_t>(3)) + 4 * sw;
       }
-      wait_lgkm0();
-      dma_tile(gp, slot_addr(x), std::make_integer_sequence<int, Kv<KF>::kNdmaX4>{});
+      issue_x4(x);
 #pragma unroll
-      for (int i2 = 0; i2 < 3; ++i2)
-        dma_b32(ksc + ((18 * srow[i2]) & ~static_cast<int64_t>(3)) + 4 * sw[i2], sc_addr(x) + 256u * i2);
-      if (hh == 0) lds_st<uint8_t>(static_cast<int>(par_addr(x)) + tdma, static_cast<uint8_t>(row & 1));
+      for (int i2 = 0; i2 < 3; ++i2) dma_b32(sp[i2], sc_addr(x) + 256u * i2);
     } else {
-      wait_lgkm0();
-      dma_tile(gp, slot_addr(x), std::make_integer_sequence<int, Kv<KF>::kNdmaX4>{});
+      issue_x4(x);
     }
   };
 
@@ -399,29 +457,36 @@ void stage1_kernel(Stage1Args a) {
     i32x2_t vv[KF == FFP8 ? 32 : 1];
     const int tvj = (lane & 15) >> 1;
     const int tv8 = tvj < 4 ? 4 * g + tvj : 16 + 4 * g + (tvj - 4);
-    const int vbe = tb + 16 * swz(tv8) + 8 * (lane & 1);
-    const int vbo = tb + 512 + 16 * (swz(tv8) ^ 4) + 8 * (lane & 1);
+    // unit c of token tv8 sits at chunk 4(c>>2) + ((c&3) ^ tswz): four lane
+    // bases, the rest is an immediate offset
+    int vb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vb[r] = tb + 16 * (tv8 * U + (r ^ tswz<KF>(tv8))) + 8 * (lane & 1);
     auto tr8_frag = [&](int c) {
       return __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<__attribute__((address_space(3))) i32x2_t*>(
-          static_cast<uintptr_t>((c & 1 ? vbo : vbe) + 1024 * (c >> 1))));
+          static_cast<uintptr_t>(vb[c & 3] + 64 * (c >> 2))));
     };
+    // QK fragment of token t, unit 4c + g (any unit index of that form keeps
+    // the swizzle inside its low two bits)
+    const int qb0 = tb + 16 * (tq0 * U + (g ^ tswz<KF>(tq0)));
+    const int qb1 = tb + 16 * (tq1 * U + (g ^ tswz<KF>(tq1)));
+    auto qoff = [&](int t, int c) { return (t == tq0 ? qb0 : qb1) + 64 * c; };
     // ---------------- QK^T: both 16-token tiles at once (two independent
     // accumulator chains), every LDS fragment fetched before the MFMAs run.
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const int ko0 = 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(tq0) ^ ((g & 1) << 2));
-    const int ko1 = 1024 * (g >> 1) + 512 * (g & 1) + 16 * (swz(tq1) ^ ((g & 1) << 2));
     if constexpr (KF == FBF16) {
 #pragma unroll
       for (int hh2 = 0; hh2 < 2; ++hh2) {
         bf16x8_t k0[9], k1[9];
 #pragma unroll
         for (int i = 0; i < 9; ++i) {
-          k0[i] = lds_ld<bf16x8_t>(tb + ko0 + 2048 * (9 * hh2 + i));
-          k1[i] = lds_ld<bf16x8_t>(tb + ko1 + 2048 * (9 * hh2 + i));
+          k0[i] = lds_ld<bf16x8_t>(qoff(tq0, 9 * hh2 + i));
+          k1[i] = lds_ld<bf16x8_t>(qoff(tq1, 9 * hh2 + i));
         }
         sched_fence();
 #pragma unroll
         for (int i = 0; i < 9; ++i) {
+          pin2(k0[i], k1[i]);
           s0 = mfma_bf16(k0[i], qb[9 * hh2 + i], s0);
           s1 = mfma_bf16(k1[i], qb[9 * hh2 + i], s1);
         }
@@ -430,40 +495,39 @@ void stage1_kernel(Stage1Args a) {
       i32x4_t k0[9], k1[9];
 #pragma unroll
       for (int c = 0; c < 9; ++c) {
-        k0[c] = lds_ld<i32x4_t>(tb + ko0 + 2048 * c);
-        k1[c] = lds_ld<i32x4_t>(tb + ko1 + 2048 * c);
+        k0[c] = lds_ld<i32x4_t>(qoff(tq0, c));
+        k1[c] = lds_ld<i32x4_t>(qoff(tq1, c));
       }
-      // the P*V fragments do not depend on the softmax: fetch them now too
-#pragma unroll
-      for (int c = 0; c < 32; ++c) vv[c] = tr8_frag(c);
       sched_fence();
 #pragma unroll
       for (int c = 0; c < 9; ++c) {
+        pin2(k0[c], k1[c]);
         s0 = mfma_bf16(cvt_fp8x8(i32x2_t{k0[c].x, k0[c].y}), qb[2 * c], s0);
         s1 = mfma_bf16(cvt_fp8x8(i32x2_t{k1[c].x, k1[c].y}), qb[2 * c], s1);
         s0 = mfma_bf16(cvt_fp8x8(i32x2_t{k0[c].z, k0[c].w}), qb[2 * c + 1], s0);
         s1 = mfma_bf16(cvt_fp8x8(i32x2_t{k1[c].z, k1[c].w}), qb[2 * c + 1], s1);
       }
     } else if constexpr (KF == FFP8) {  // fp8 x fp8
-      const int e0 = tb + 1024 * g + 16 * swz(tq0), o0 = tb + 1024 * g + 512 + 16 * (swz(tq0) ^ 4);
-      const int e1 = tb + 1024 * g + 16 * swz(tq1), o1 = tb + 1024 * g + 512 + 16 * (swz(tq1) ^ 4);
       i32x8_t a0[5], a1[5];
 #pragma unroll
       for (int c = 0; c < 5; ++c) {
         a0[c] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
         a1[c] = a0[c];
         if (c < 4 || g < 2) {
-          const i32x4_t u0 = lds_ld<i32x4_t>(e0 + 4096 * c), u1 = lds_ld<i32x4_t>(o0 + 4096 * c);
-          const i32x4_t w0 = lds_ld<i32x4_t>(e1 + 4096 * c), w1 = lds_ld<i32x4_t>(o1 + 4096 * c);
+          // units 8c + 2g + {0,1}: the swizzle touches only their low two bits
+          const int f0 = tswz<KF>(tq0), f1 = tswz<KF>(tq1);
+          const i32x4_t u0 = lds_ld<i32x4_t>(tb + 16 * (tq0 * U + 8 * c + ((2 * g) ^ f0)));
+          const i32x4_t u1 = lds_ld<i32x4_t>(tb + 16 * (tq0 * U + 8 * c + ((2 * g + 1) ^ f0)));
+          const i32x4_t w0 = lds_ld<i32x4_t>(tb + 16 * (tq1 * U + 8 * c + ((2 * g) ^ f1)));
+          const i32x4_t w1 = lds_ld<i32x4_t>(tb + 16 * (tq1 * U + 8 * c + ((2 * g + 1) ^ f1)));
           a0[c] = i32x8_t{u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
           a1[c] = i32x8_t{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         }
       }
-#pragma unroll
-      for (int c = 0; c < 32; ++c) vv[c] = tr8_frag(c);
       sched_fence();
 #pragma unroll
       for (int c = 0; c < 5; ++c) {
+        pin2(a0[c], a1[c]);
         s0 = mfma_fp8(a0[c], q8[c], s0);
         s1 = mfma_fp8(a1[c], q8[c], s1);
       }
@@ -476,21 +540,22 @@ void stage1_kernel(Stage1Args a) {
         uint32_t r0[2], r1[2], c0[6], c1[6];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          u0[c] = lds_ld<i32x4_t>(tb + ko0 + 2048 * c);
-          u1[c] = lds_ld<i32x4_t>(tb + ko1 + 2048 * c);
+          u0[c] = lds_ld<i32x4_t>(qoff(tq0, c));
+          u1[c] = lds_ld<i32x4_t>(qoff(tq1, c));
           c0[c] = lds_ld<uint8_t>(sb0 + 4 * c + g);
           c1[c] = lds_ld<uint8_t>(sb1 + 4 * c + g);
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          r0[e] = lds_ld<uint32_t>(tb + 8192 + 512 * e + 16 * (swz(tq0) ^ (e << 2)) + 4 * g);
-          r1[e] = lds_ld<uint32_t>(tb + 8192 + 512 * e + 16 * (swz(tq1) ^ (e << 2)) + 4 * g);
+          r0[e] = lds_ld<uint32_t>(tb + 16 * (tq0 * U + 16 + e) + 4 * g);
+          r1[e] = lds_ld<uint32_t>(tb + 16 * (tq1 * U + 16 + e) + 4 * g);
           c0[4 + e] = lds_ld<uint8_t>(sb0 + 16 + e);
           c1[4 + e] = lds_ld<uint8_t>(sb1 + 16 + e);
         }
         sched_fence();
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
+          pin2(u0[c], u1[c]);
           const float f0 = e8m0_f32(c0[c]), f1 = e8m0_f32(c1[c]);
           s0 = mfma_bf16(cvt_fp4x8(u0[c].x, f0), qb[4 * c + 0], s0);
           s1 = mfma_bf16(cvt_fp4x8(u1[c].x, f1), qb[4 * c + 0], s1);
@@ -511,8 +576,8 @@ void stage1_kernel(Stage1Args a) {
         uint32_t c0[5], c1[5];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          u0[c] = lds_ld<i32x4_t>(tb + ko0 + 2048 * c);
-          u1[c] = lds_ld<i32x4_t>(tb + ko1 + 2048 * c);
+          u0[c] = lds_ld<i32x4_t>(qoff(tq0, c));
+          u1[c] = lds_ld<i32x4_t>(qoff(tq1, c));
           c0[c] = lds_ld<uint8_t>(sb0 + 4 * c + g);
           c1[c] = lds_ld<uint8_t>(sb1 + 4 * c + g);
         }
@@ -521,14 +586,15 @@ void stage1_kernel(Stage1Args a) {
         c0[4] = 127u;
         c1[4] = 127u;
         if (g < 2) {
-          u0[4] = lds_ld<i32x4_t>(tb + 8192 + 512 * g + 16 * (swz(tq0) ^ (g << 2)));
-          u1[4] = lds_ld<i32x4_t>(tb + 8192 + 512 * g + 16 * (swz(tq1) ^ (g << 2)));
+          u0[4] = lds_ld<i32x4_t>(tb + 16 * (tq0 * U + 16 + g));
+          u1[4] = lds_ld<i32x4_t>(tb + 16 * (tq1 * U + 16 + g));
           c0[4] = lds_ld<uint8_t>(sb0 + 16 + g);
           c1[4] = lds_ld<uint8_t>(sb1 + 16 + g);
         }
         sched_fence();
 #pragma unroll
         for (int c = 0; c < 5; ++c) {
+          pin2(u0[c], u1[c]);
           s0 = mfma_fp4(u0[c], c0[c], q4[c], q4s[c], s0);
           s1 = mfma_fp4(u1[c], c1[c], q4[c], q4s[c], s1);
         }
@@ -573,17 +639,20 @@ void stage1_kernel(Stage1Args a) {
       const int j = lane & 15;
       const int kb = (j & 3) >> 1;
       const int ta = 4 * g + (j >> 2), tc = 16 + 4 * g + (j >> 2);
-      const int ba = tb + 512 * kb + 16 * (swz(ta) ^ (kb << 2)) + 8 * (j & 1);
-      const int bc = tb + 512 * kb + 16 * (swz(tc) ^ (kb << 2)) + 8 * (j & 1);
+
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg) {
         i16x4_t v0[8], v1[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           v0[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(static_cast<uintptr_t>(ba + 1024 * (8 * cg + e))));
+              reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(
+                  static_cast<uintptr_t>(tb + 16 * (ta * U + 4 * ((8 * cg + e) >> 1) +
+                                                   ((2 * ((8 * cg + e) & 1) + kb) ^ tswz<KF>(ta))) + 8 * (j & 1))));
           v1[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(static_cast<uintptr_t>(bc + 1024 * (8 * cg + e))));
+              reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(
+                  static_cast<uintptr_t>(tb + 16 * (tc * U + 4 * ((8 * cg + e) >> 1) +
+                                                   ((2 * ((8 * cg + e) & 1) + kb) ^ tswz<KF>(tc))) + 8 * (j & 1))));
         }
         sched_fence();
 #pragma unroll
@@ -593,8 +662,19 @@ void stage1_kernel(Stage1Args a) {
         }
       }
     } else if constexpr (KF == FFP8) {
+      // four groups of eight 16-column tiles, two groups of reads in flight
 #pragma unroll
-      for (int c = 0; c < 32; ++c) acc[c] = mfma_bf16(cvt_fp8x8(vv[c]), pb, acc[c]);
+      for (int c = 0; c < 16; ++c) vv[c] = tr8_frag(c);
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        pin8(vv + 8 * cg);
+        if (cg < 2) {
+#pragma unroll
+          for (int c = 16 + 8 * cg; c < 24 + 8 * cg; ++c) vv[c] = tr8_frag(c);
+        }
+#pragma unroll
+        for (int c = 8 * cg; c < 8 * cg + 8; ++c) acc[c] = mfma_bf16(cvt_fp8x8(vv[c]), pb, acc[c]);
+      }
     } else {
       // mxfp4: lane (column block i = lane&15) decodes unit i of its 8 tokens;
       // output tile c row r <-> latent column 32*(4g+r) + c.
@@ -606,7 +686,7 @@ void stage1_kernel(Stage1Args a) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int tv = kk < 4 ? 4 * g + kk : 16 + 4 * g + (kk - 4);
-        const i32x4_t u = lds_ld<i32x4_t>(tb + unit_off(tv, i));
+        const i32x4_t u = lds_ld<i32x4_t>(tb + 16 * (tv * U + i));
         vw[kk][0] = u.x;
         vw[kk][1] = u.y;
         vw[kk][2] = u.z;
