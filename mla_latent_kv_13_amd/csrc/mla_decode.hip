@@ -159,6 +159,13 @@ template <class T>
 __device__ __forceinline__ void pin2(T& a, T& b) {
   asm volatile("" : "+v"(a), "+v"(b) : : "memory");
 }
+// Keep eight accumulator tiles in AGPRs at this point.  The O accumulator is
+// only touched by MFMA except in the rare rescale branch; without this the
+// loop-carried value is kept in VGPRs and copied both ways every iteration.
+template <class T>
+__device__ __forceinline__ void pin_acc8(T* v) {
+  asm volatile("" : "+a"(v[0]), "+a"(v[1]), "+a"(v[2]), "+a"(v[3]), "+a"(v[4]), "+a"(v[5]), "+a"(v[6]), "+a"(v[7]));
+}
 template <class T>
 __device__ __forceinline__ void pin8(T* v) {
   asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
@@ -615,12 +622,16 @@ void stage1_kernel(Stage1Args a) {
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmax3(mx, sv[i]);
     mx = group_max(mx);
+#pragma unroll
+    for (int c = 0; c < 32; c += 8) pin_acc8(acc + c);
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmax3(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int c = 0; c < 32; ++c) acc[c] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 32; c += 8) pin_acc8(acc + c);
       m_run = m_new;
     }
     u32x4_t pw;
