@@ -4,18 +4,20 @@
 A "step" is one mla_decode call (stage 1 + stage 2 when S > 1) over one batch
 of synthetic inputs already resident in HBM.  The headline workload is
 bs=256, kv_len=8192, bf16 Q over an fp8 e4m3fn paged cache (page 8, shuffled
-pages), where the 70%-of-HBM-peak target is stated.  `value` is achieved
+pages); at one split per request a call is a single stage-1 launch, so the
+per-call event time is that kernel's launch duration.  `value` is achieved
 GB/s of compulsory traffic (cache incl. scales + Q + page table + indptr +
 output) per second; split-K partials are not credited.  The remaining
 workloads (the five benchmark shapes) are timed too and listed under
 "workloads", each with rotated buffer replicas when its working set would fit
 the 256 MB Infinity Cache.
 
-Prints ONE JSON line.  --gpus must be 1 (this build runs on a single GPU).
+Prints ONE JSON line.  --gpus must be 1: the decode path runs on a single GPU.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -33,6 +35,38 @@ from mla_latent_kv_13_amd import synth  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bs256_kv8192_a16w8"
 FMT = {"bf16": mla.BF16, "fp8": mla.FP8, "mxfp4": mla.MXFP4}
+FLOPS_PER_TOKEN = 2 * 16 * (576 + 512)  # QK^T and P*V multiply-adds, all 16 heads
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense
+KERNEL_SOURCE = os.path.join(REPO, "mla_latent_kv_13_amd", "csrc", "mla_decode.hip")
+TRAFFIC_FILE = os.path.join(REPO, "profiles", "stage1_a16w8_bs256_kv8192_hbm_traffic.txt")
+
+
+def kernel_source_sha256() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per stage-1 launch from the committed FETCH_SIZE/WRITE_SIZE summary.
+
+    Only reported for the workload the counters were taken on, and only while
+    the kernel source is byte-identical to the one they were taken from (the
+    summary records its sha256); otherwise None.
+    """
+    if workload != HEADLINE or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            k, sep, v = line.strip().partition(":")
+            if sep and v.split():
+                fields[k.strip()] = v.split()[0]
+    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def compulsory_bytes(w, page_size) -> int:
@@ -71,25 +105,13 @@ def replicate(ops, n):
     return reps
 
 
-def time_workload(w, steps, warmup, device):
-    S = w.num_splits or mla.choose_num_splits(w.batch, w.kv_len, FMT[w.kv_fmt])
-    ops = build_inputs(w, device)
-    ws_bytes = mla.workspace_bytes(w.batch, S)
-    work = sum(v.numel() * v.element_size() for v in ops.values() if v is not None) + ws_bytes + w.batch * 16 * 1024
-    nrep = 1 if work >= (512 << 20) else min(256, max(2, math.ceil((1 << 30) / work)))
-    reps = replicate(ops, nrep)
-    for r in reps:
-        r["out"] = torch.empty((w.batch, 16, 512), dtype=torch.bfloat16, device=device)
-        r["ws"] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device) if ws_bytes else None
-
-    def call(i):
-        r = reps[i % nrep]
-        mla.decode(r["q"], r["kv"], r["kv_indptr"], r["page_table"], w.page_size, S, q_scale=r["q_scale"],
-                   kv_scale=r["kv_scale"], out=r["out"], workspace=r["ws"])
-
-    # warm up for at least `warmup` calls and ~0.3 s, so clocks and caches settle
+def time_calls(call, steps, warmup, warmup_s):
+    """Warm up, then time `steps` calls in five back-to-back groups with HIP
+    events on the launch stream.  Returns (median, min, max) ms per call over
+    the groups and the host wall time per call."""
+    # warm up for at least `warmup` calls and `warmup_s` seconds, so clocks settle
     i = 0
-    t_end = time.perf_counter() + 0.3
+    t_end = time.perf_counter() + warmup_s
     while i < warmup or time.perf_counter() < t_end:
         call(i)
         i += 1
@@ -97,8 +119,6 @@ def time_workload(w, steps, warmup, device):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    # `steps` timed calls, in five back-to-back groups timed with HIP events on
-    # the launch stream; the headline is the median group (per call)
     ngroups = 5
     per = max(1, steps // ngroups)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ngroups)]
@@ -113,21 +133,67 @@ def time_workload(w, steps, warmup, device):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / (ngroups * per)
     group_ms = sorted(e0.elapsed_time(e1) / per for e0, e1 in evs)
-    ev_ms = group_ms[len(group_ms) // 2]
+    return group_ms[len(group_ms) // 2], group_ms[0], group_ms[-1], wall
+
+
+def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
+    """Time one workload with its stated split count on rotated buffer replicas
+    (the headline figure).  With `extras`, also time it on one set of buffers
+    (warm, Infinity-Cache resident when small) and with the library heuristic's
+    split count when that differs."""
+    S = w.num_splits or mla.choose_num_splits(w.batch, w.kv_len, FMT[w.kv_fmt])
+    S_heur = mla.choose_num_splits(w.batch, w.kv_len, FMT[w.kv_fmt])
+    ops = build_inputs(w, device)
+    ws_bytes = max(mla.workspace_bytes(w.batch, S), mla.workspace_bytes(w.batch, S_heur))
+    work = sum(v.numel() * v.element_size() for v in ops.values() if v is not None) + ws_bytes + w.batch * 16 * 1024
+    nrep = 1 if work >= (512 << 20) else min(256, max(2, math.ceil((1 << 30) / work)))
+    reps = replicate(ops, nrep)
+    for r in reps:
+        r["out"] = torch.empty((w.batch, 16, 512), dtype=torch.bfloat16, device=device)
+        r["ws"] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device) if ws_bytes else None
+
+    def caller(nsplit, nr):
+        def call(i):
+            r = reps[i % nr]
+            mla.decode(r["q"], r["kv"], r["kv_indptr"], r["page_table"], w.page_size, nsplit, q_scale=r["q_scale"],
+                       kv_scale=r["kv_scale"], out=r["out"], workspace=r["ws"])
+        return call
+
+    ev_ms, mn, mx, wall = time_calls(caller(S, nrep), steps, warmup, warmup_s)
     nbytes = compulsory_bytes(w, w.page_size)
     res = {
         "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q": w.q_fmt, "kv": w.kv_fmt,
         "page_size": w.page_size, "num_splits": S, "replicas": nrep,
-        "us_per_call": round(ev_ms * 1e3, 3), "us_min": round(group_ms[0] * 1e3, 3),
-        "us_max": round(group_ms[-1] * 1e3, 3), "wall_us_per_call": round(wall * 1e6, 3),
+        "us_per_call": round(ev_ms * 1e3, 3), "us_min": round(mn * 1e3, 3),
+        "us_max": round(mx * 1e3, 3), "wall_us_per_call": round(wall * 1e6, 3),
         "compulsory_bytes": nbytes, "gbs": round(nbytes / (ev_ms * 1e-3) / 1e9, 1),
         "frac_of_peak": round(nbytes / (ev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "partial_bytes": 2 * ws_bytes,
-        "tflops": round(2 * 16 * w.batch * w.kv_len * (576 + 512) / (ev_ms * 1e-3) / 1e12, 2),
+        "partial_bytes": 2 * mla.workspace_bytes(w.batch, S),
+        "tflops": round(FLOPS_PER_TOKEN * w.batch * w.kv_len / (ev_ms * 1e-3) / 1e12, 2),
     }
+    if extras and nrep > 1:
+        warm = time_calls(caller(S, 1), steps, warmup, 0.05)[0]
+        res["us_warm_same_buffers"] = round(warm * 1e3, 3)
+    if extras and S_heur != S:
+        heur = time_calls(caller(S_heur, nrep), steps, warmup, 0.05)[0]
+        res["heuristic_num_splits"] = S_heur
+        res["us_heuristic_splits"] = round(heur * 1e3, 3)
     del reps, ops
     torch.cuda.empty_cache()
     return res, wall
+
+
+def read_ceiling(nbytes, device, steps=50):
+    """Median GB/s of the library's streaming-read probe over a buffer of
+    `nbytes` bytes: the practical HBM read ceiling for a read-once kernel."""
+    nbytes = (nbytes + 15) // 16 * 16
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=device)
+    ms = time_calls(lambda i: mla.stream_read(buf, sink), steps, 10, 0.2)[0]
+    del buf
+    torch.cuda.empty_cache()
+    return round(nbytes / (ms * 1e-3) / 1e9, 1), round(ms * 1e3, 3)
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -182,13 +248,15 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=list(synth.WORKLOADS))
     ap.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warmup-seconds", type=float, default=0.3,
+                    help="minimum warm-up time per workload (0 for short profiled runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of decoding, run a plain device-to-device copy of this many bytes "
                          "(the known-size reference used to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(requests shard across GPUs with no communication; see the design notes).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the decode path has no multi-GPU mode "
+              "(requests would shard across GPUs by batch, with no communication).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -211,14 +279,16 @@ def main():
         return
     w = synth.WORKLOADS[args.workload]
     print(f"[bench] headline {w.name}", file=sys.stderr, flush=True)
-    head, wall = time_workload(w, args.steps, args.warmup, device)
+    head, wall = time_workload(w, args.steps, args.warmup, device, args.warmup_seconds, extras=False)
+    print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
+    ceil_gbs, ceil_us = read_ceiling(head["compulsory_bytes"], device)
     others = []
     if not args.only_headline:
         for name, ow in synth.WORKLOADS.items():
             if name == w.name:
                 continue
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            others.append(time_workload(ow, max(10, args.steps // 2), args.warmup, device)[0])
+            others.append(time_workload(ow, max(10, args.steps // 2), args.warmup, device, args.warmup_seconds)[0])
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -240,8 +310,15 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 Q and cache rows, quantised on the GPU)",
         "config": {"workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q": w.q_fmt, "kv": w.kv_fmt,
                    "page_size": w.page_size, "num_splits": head["num_splits"], "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": head["frac_of_peak"], "traffic": None},
+        "roofline": {"kernel": "stage1_kernel" + ("" if head["num_splits"] == 1 else " + stage2_kernel"),
+                     "bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": head["frac_of_peak"], "traffic": measured_traffic(w.name),
+                     "traffic_unit": "bytes per launch",
+                     "read_ceiling": {"achieved": ceil_gbs, "us": ceil_us, "bytes": head["compulsory_bytes"],
+                                      "kernel": "stream_read_kernel (16-B non-temporal loads, read once)"},
+                     "frac_of_read_ceiling": round(head["gbs"] / ceil_gbs, 4)},
+        "mfma": {"dtype": "bf16" if w.kv_fmt != "mxfp4" else "bf16/fp4", "achieved_tflops": head["tflops"],
+                 "peak_tflops": PEAK_MFMA_BF16_TFLOPS, "frac": round(head["tflops"] / PEAK_MFMA_BF16_TFLOPS, 4)},
         "cpu_baseline": cpu,
         "workloads": [head] + others,
     }

@@ -162,6 +162,18 @@ int mla_quantize_fp8(const void* src_bf16, int64_t n, uint8_t* dst, float* scale
 int mla_quantize_mxfp4(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* packed,
                        uint8_t* scales, void* stream);
 
+/*
+ * mla_stream_read - measurement helper, not part of the decode path.  Reads
+ * `bytes` bytes (a multiple of 16) of the device buffer `src` (16-byte
+ * aligned) once with 16-byte non-temporal loads spread over up to 16384
+ * workgroups, folding them into one word that is written to `sink` (device,
+ * 4 bytes) only if it equals a fixed improbable value.  Enqueued on `stream`;
+ * its duration is the streaming-read ceiling of the device for a buffer of
+ * that size.  Returns MLA_ERR_ARG for a negative or unaligned size,
+ * MLA_ERR_NULL, MLA_ERR_ALIGN or MLA_ERR_LAUNCH; 0 bytes is a no-op.
+ */
+int mla_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* mla_status_string(int status);
 

@@ -43,8 +43,8 @@ _DECODE_ARGS = [_c_void, _c_int32, _c_void, _c_void, _c_int32, _c_void, _c_int64
                 _c_void, _c_void, _c_int32, _c_int32, _c_void, _c_void, _c_size]
 
 EXPORTS = ("mla_decode", "mla_validate", "mla_workspace_bytes", "mla_choose_num_splits",
-           "mla_recommend_page_size", "mla_quantize_fp8", "mla_quantize_mxfp4", "mla_status_string",
-           "mla_abi_version")
+           "mla_recommend_page_size", "mla_quantize_fp8", "mla_quantize_mxfp4", "mla_stream_read",
+           "mla_status_string", "mla_abi_version")
 
 
 class StatusError(RuntimeError):
@@ -77,6 +77,8 @@ def load():
             L.mla_quantize_fp8.argtypes = [_c_void, _c_int64, _c_void, _c_void, _c_int32, _c_void]
             L.mla_quantize_mxfp4.restype = ctypes.c_int
             L.mla_quantize_mxfp4.argtypes = [_c_void, _c_int64, _c_int64, _c_void, _c_void, _c_void]
+            L.mla_stream_read.restype = ctypes.c_int
+            L.mla_stream_read.argtypes = [_c_void, _c_int64, _c_void, _c_void]
             L.mla_status_string.restype = ctypes.c_char_p
             L.mla_status_string.argtypes = [ctypes.c_int]
             L.mla_abi_version.restype = _c_int32
@@ -223,3 +225,16 @@ def quantize_mxfp4(x: torch.Tensor, stream=None):
     if rc:
         raise StatusError("mla_quantize_mxfp4", rc)
     return packed, scales
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue one streaming read of the whole of `buf` (measurement helper;
+    `sink` is a 4-byte device tensor that the kernel almost never writes)."""
+    _dev(buf)
+    _dev(sink)
+    if not buf.is_contiguous():
+        raise ValueError("stream_read needs a contiguous buffer")
+    nbytes = buf.numel() * buf.element_size()
+    rc = load().mla_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(stream))
+    if rc:
+        raise StatusError("mla_stream_read", rc)

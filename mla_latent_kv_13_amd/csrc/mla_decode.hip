@@ -31,6 +31,7 @@
 //     writes bf16 out directly, otherwise fp32 partial O / base-2 LSE.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <utility>
 
@@ -1023,6 +1024,30 @@ int grid_for(int64_t n, int per) {
   return static_cast<int>(g);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming-read probe: each workgroup reads one contiguous chunk with 16-byte
+// non-temporal loads, four per lane in flight, and folds them into one word.
+// The word is stored only if it equals an improbable constant, so the loads
+// stay live without adding writes.  Measures the HBM read ceiling that the
+// decode kernels (which read their cache once) are compared against.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src, int64_t n16,
+                                                          int64_t per_block, uint32_t* sink) {
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * per_block;
+  const int64_t b1 = min(b0 + per_block, n16);
+  uint32_t acc = 0;
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += 4 * 256) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = i + 256 * u;
+      v[u] = j < b1 ? __builtin_nontemporal_load(src + j) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1096,6 +1121,23 @@ int mla_quantize_mxfp4(const void* src_bf16, int64_t rows, int64_t cols, uint8_t
   if (grid > 0x7fffffffLL) return MLA_ERR_ARG;
   hipLaunchKernelGGL(quant_mxfp4_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, static_cast<const uint16_t*>(src_bf16),
                      nblocks, cols, packed, scales);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int mla_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16) return MLA_ERR_ARG;
+  if (bytes == 0) return MLA_OK;
+  if (!src || !sink) return MLA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(src) & 15u) return MLA_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int64_t n16 = bytes / 16;
+  // 64 workgroups per CU of 256-thread blocks: enough loads in flight to
+  // saturate HBM on every XCD.
+  const int64_t grid = std::min<int64_t>(16384, (n16 + 1023) / 1024);
+  const int64_t per_block = (n16 + grid - 1) / grid;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                     static_cast<const u32x4_t*>(src), n16, per_block, sink);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 

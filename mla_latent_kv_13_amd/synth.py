@@ -35,7 +35,7 @@ class Workload:
 
 
 # The five benchmark shapes (bs x kv_len x precision mix) plus the bs=256 fp8
-# shape at which the 70%-of-HBM-peak target is stated.
+# shape, the long-context HBM-bound headline case.
 WORKLOADS = {
     w.name: w
     for w in [

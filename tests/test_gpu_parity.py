@@ -152,7 +152,7 @@ def test_decode_matches_oracle(orc, qf, kf, shape):
     ref, _ = oracle_decode(case, o, orc)
     check_close(out, ref, what=f"{qf}/{kf} shape {shape}")
     # The 0.1/0.1 check against the unquantised cache measures the format's own
-    # error, which the pages judge on benchmark-length sequences.  An mxfp4 row
+    # error, which the pages assess on benchmark-length sequences.  An mxfp4 row
     # carries element errors up to a quarter of its block max, and short requests
     # average over too few rows to stay inside 0.1, so for mxfp4 that check runs
     # on the full-size 8192-token workloads (test_full_size_workload) only.

@@ -107,6 +107,16 @@ def test_split_heuristic(lib):
     assert mla.choose_num_splits(32, 1024, mla.FP8) >= 4
 
 
+def test_stream_read_argument_errors(lib):
+    # every one of these is rejected (or is a no-op) before anything is launched
+    assert lib.mla_stream_read(A, 0, A2, None) == 0
+    assert lib.mla_stream_read(A, -16, A2, None) == -3
+    assert lib.mla_stream_read(A, 24, A2, None) == -3
+    assert lib.mla_stream_read(None, 64, A2, None) == -1
+    assert lib.mla_stream_read(A, 64, None, None) == -1
+    assert lib.mla_stream_read(A + 4, 64, A2, None) == -4
+
+
 def test_page_size_recommendation(lib):
     assert mla.recommend_page_size(4, 1024) >= 1
     assert mla.recommend_page_size(256, 8192) >= 1
