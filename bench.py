@@ -2,7 +2,9 @@
 """MLA decode benchmark on one MI355X: microseconds per call and achieved HBM GB/s.
 
 A "step" is one mla_decode call (stage 1 + stage 2 when S > 1) over one batch
-of synthetic inputs already resident in HBM.  The headline workload is
+of synthetic inputs already resident in HBM.  Calls are captured into a HIP
+graph and replayed, as a serving loop issues decode, so short calls measure
+the GPU rather than the Python launch path.  The headline workload is
 bs=256, kv_len=8192, bf16 Q over an fp8 e4m3fn paged cache (page 8, shuffled
 pages); at one split per request a call is a single stage-1 launch, so the
 per-call event time is that kernel's launch duration.  `value` is achieved
@@ -105,35 +107,51 @@ def replicate(ops, n):
     return reps
 
 
-def time_calls(call, steps, warmup, warmup_s):
-    """Warm up, then time `steps` calls in five back-to-back groups with HIP
-    events on the launch stream.  Returns (median, min, max) ms per call over
-    the groups and the host wall time per call."""
-    # warm up for at least `warmup` calls and `warmup_s` seconds, so clocks settle
-    i = 0
-    t_end = time.perf_counter() + warmup_s
-    while i < warmup or time.perf_counter() < t_end:
-        call(i)
-        i += 1
-        if i % 32 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+def time_calls(call, steps, warmup, warmup_s, per_graph=None):
+    """Time `steps` calls (rounded to whole graphs) replayed from a HIP graph.
+
+    The calls are captured once into a graph of `per_graph` consecutive calls
+    (call(i) for i in [0, per_graph)), so the GPU sees back-to-back kernels with
+    no host launch overhead -- the way a serving loop issues decode.  After a
+    warm-up of at least `warmup` calls and `warmup_s` seconds, five groups of
+    whole graph replays are timed with HIP events on the launch stream.
+    Returns (median, min, max) ms per call over the groups, the host wall time
+    per call and the number of timed calls."""
     ngroups = 5
-    per = max(1, steps // ngroups)
+    per_graph = per_graph or max(1, steps // ngroups)
+    reps_per_group = max(1, math.ceil(steps / (ngroups * per_graph)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # eager calls first: nothing is lazily initialised inside the capture
+        for i in range(per_graph):
+            call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(per_graph):
+            call(i)
+    torch.cuda.synchronize()
+    n = 0
+    t_end = time.perf_counter() + warmup_s
+    while n < warmup or time.perf_counter() < t_end:
+        graph.replay()
+        n += per_graph
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ngroups)]
     t0 = time.perf_counter()
-    k = i
     for r in range(ngroups):
         evs[r][0].record(stream)
-        for _ in range(per):
-            call(k)
-            k += 1
+        for _ in range(reps_per_group):
+            graph.replay()
         evs[r][1].record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / (ngroups * per)
-    group_ms = sorted(e0.elapsed_time(e1) / per for e0, e1 in evs)
-    return group_ms[len(group_ms) // 2], group_ms[0], group_ms[-1], wall
+    calls = ngroups * reps_per_group * per_graph
+    wall = (time.perf_counter() - t0) / calls
+    group_ms = sorted(e0.elapsed_time(e1) / (reps_per_group * per_graph) for e0, e1 in evs)
+    del graph
+    return group_ms[len(group_ms) // 2], group_ms[0], group_ms[-1], wall, calls
 
 
 def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
@@ -159,11 +177,12 @@ def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
                        kv_scale=r["kv_scale"], out=r["out"], workspace=r["ws"])
         return call
 
-    ev_ms, mn, mx, wall = time_calls(caller(S, nrep), steps, warmup, warmup_s)
+    per_graph = nrep if nrep > 1 else None
+    ev_ms, mn, mx, wall, calls = time_calls(caller(S, nrep), steps, warmup, warmup_s, per_graph)
     nbytes = compulsory_bytes(w, w.page_size)
     res = {
         "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q": w.q_fmt, "kv": w.kv_fmt,
-        "page_size": w.page_size, "num_splits": S, "replicas": nrep,
+        "page_size": w.page_size, "num_splits": S, "replicas": nrep, "timed_calls": calls,
         "us_per_call": round(ev_ms * 1e3, 3), "us_min": round(mn * 1e3, 3),
         "us_max": round(mx * 1e3, 3), "wall_us_per_call": round(wall * 1e6, 3),
         "compulsory_bytes": nbytes, "gbs": round(nbytes / (ev_ms * 1e-3) / 1e9, 1),
@@ -172,10 +191,10 @@ def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
         "tflops": round(FLOPS_PER_TOKEN * w.batch * w.kv_len / (ev_ms * 1e-3) / 1e12, 2),
     }
     if extras and nrep > 1:
-        warm = time_calls(caller(S, 1), steps, warmup, 0.05)[0]
+        warm = time_calls(caller(S, 1), steps, warmup, 0.05, min(nrep, 64))[0]
         res["us_warm_same_buffers"] = round(warm * 1e3, 3)
     if extras and S_heur != S:
-        heur = time_calls(caller(S_heur, nrep), steps, warmup, 0.05)[0]
+        heur = time_calls(caller(S_heur, nrep), steps, warmup, 0.05, per_graph)[0]
         res["heuristic_num_splits"] = S_heur
         res["us_heuristic_splits"] = round(heur * 1e3, 3)
     del reps, ops
@@ -308,6 +327,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.q_fmt == "bf16" else w.q_fmt,
         "data": "synthetic (seeded N(0,1) bf16 Q and cache rows, quantised on the GPU)",
+        "launch": "HIP graph replay of back-to-back mla_decode calls",
         "config": {"workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q": w.q_fmt, "kv": w.kv_fmt,
                    "page_size": w.page_size, "num_splits": head["num_splits"], "parallelism": "single GPU"},
         "roofline": {"kernel": "stage1_kernel" + ("" if head["num_splits"] == 1 else " + stage2_kernel"),

@@ -164,11 +164,12 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
         num_splits = choose_num_splits(batch, hint, _fmt(kv_cache))
     if out is None:
         out = torch.empty((batch, HEADS, D_V), dtype=torch.bfloat16, device=kv_cache.device)
-    need = workspace_bytes(batch, num_splits) if batch > 0 else 0
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=kv_cache.device)
+    if workspace is None and batch > 0:
+        need = workspace_bytes(batch, num_splits)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=kv_cache.device)
     _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out, workspace)
-    rc = load().mla_decode(*_decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale,
+    rc = (_lib or load()).mla_decode(*_decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale,
                                          kv_scale, page_indptr, out, workspace), _stream(stream))
     if rc:
         raise StatusError("mla_decode", rc)

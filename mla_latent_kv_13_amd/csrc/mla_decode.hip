@@ -99,7 +99,7 @@ template <int KF> struct Lay {
   static constexpr int kRowOff = kPidOff + kNpid * kPidSlot;       // physical row per token (u32)
   static constexpr int kPtrOff = kRowOff + 4 * kSub;                // row base address per token (u64)
   static constexpr int kWaveBytes = kPtrOff + 8 * kSub;
-  static constexpr int kCombine = 2 * 128 * 64 * 4 + 2 * kWaves * kHeads * 4;
+  static constexpr int kCombine = kWaves * 32768 + 2 * kWaves * kHeads * 4;  // 4 partial O^T + (m, l)
   static constexpr int kTotal = kWaves * kWaveBytes > kCombine ? kWaves * kWaveBytes : kCombine;
   static constexpr int kNdma = Kv<KF>::kNdmaX4 + Kv<KF>::kNdmaSc;  // VMEM instrs per sub-tile
 };
@@ -290,6 +290,43 @@ void stage1_kernel(Stage1Args a) {
   const int b = blockIdx.x / S;
   const int s = blockIdx.x - b * S;
 
+  // ---- Q fragments (B operands) for this lane's head.  Issued first: they
+  // depend on the request index only, so their latency overlaps the
+  // kv_indptr load and the page-id gathers that follow.
+  constexpr int NQ = QFrag<QF, KF>::kN;
+  bf16x8_t qb[QF == FBF16 ? NQ : 1];
+  i32x8_t q8[QF == FFP8 ? NQ : 1];
+  i32x4_t q4[QF == FMX ? NQ : 1];
+  uint32_t q4s[QF == FMX ? NQ : 1];
+  float qs = 1.0f, ks = 1.0f;
+  if constexpr (QF == FBF16) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qrow + qdim_bf16<KF>(m, g));
+  } else if constexpr (QF == FFP8) {
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q8[c] = *reinterpret_cast<const i32x8_t*>(qrow + 128 * c + 32 * g);
+    q8[4] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (g < 2) q8[4] = *reinterpret_cast<const i32x8_t*>(qrow + 512 + 32 * g);
+    qs = *static_cast<const float*>(a.q_scale);
+  } else {
+    const size_t qr = static_cast<size_t>(b) * kHeads + hq;
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * MLA_MXFP4_ROW_BYTES;
+    const uint8_t* qsc = static_cast<const uint8_t*>(a.q_scale) + qr * MLA_MXFP4_ROW_SCALES;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      q4[c] = *reinterpret_cast<const i32x4_t*>(qrow + 64 * c + 16 * g);
+      q4s[c] = qsc[4 * c + g];
+    }
+    q4[4] = i32x4_t{0, 0, 0, 0};
+    q4s[4] = 127u;
+    if (g < 2) {
+      q4[4] = *reinterpret_cast<const i32x4_t*>(qrow + 256 + 16 * g);
+      q4s[4] = qsc[16 + g];
+    }
+  }
+  if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
   const int kv0 = a.kv_indptr[b];
   const int Lr = a.kv_indptr[b + 1] - kv0;
   const int chunk = (Lr + S - 1) / S;
@@ -389,48 +426,12 @@ void stage1_kernel(Stage1Args a) {
     }
   };
 
-  // The first page-id gathers go out before the Q loads so that both
-  // latencies overlap; one wait then covers them.
+  // The first page-id gathers overlap the Q loads; one wait covers both.
   if (nloc > 0) {
 #pragma unroll
     for (int X = 0; X < D; ++X) issue_pid(X);
   }
 
-  // ---- Q fragments (B operands) for this lane's head
-  constexpr int NQ = QFrag<QF, KF>::kN;
-  bf16x8_t qb[QF == FBF16 ? NQ : 1];
-  i32x8_t q8[QF == FFP8 ? NQ : 1];
-  i32x4_t q4[QF == FMX ? NQ : 1];
-  uint32_t q4s[QF == FMX ? NQ : 1];
-  float qs = 1.0f, ks = 1.0f;
-  if constexpr (QF == FBF16) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qrow + qdim_bf16<KF>(m, g));
-  } else if constexpr (QF == FFP8) {
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) q8[c] = *reinterpret_cast<const i32x8_t*>(qrow + 128 * c + 32 * g);
-    q8[4] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    if (g < 2) q8[4] = *reinterpret_cast<const i32x8_t*>(qrow + 512 + 32 * g);
-    qs = *static_cast<const float*>(a.q_scale);
-  } else {
-    const size_t qr = static_cast<size_t>(b) * kHeads + hq;
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * MLA_MXFP4_ROW_BYTES;
-    const uint8_t* qsc = static_cast<const uint8_t*>(a.q_scale) + qr * MLA_MXFP4_ROW_SCALES;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      q4[c] = *reinterpret_cast<const i32x4_t*>(qrow + 64 * c + 16 * g);
-      q4s[c] = qsc[4 * c + g];
-    }
-    q4[4] = i32x4_t{0, 0, 0, 0};
-    q4s[4] = 127u;
-    if (g < 2) {
-      q4[4] = *reinterpret_cast<const i32x4_t*>(qrow + 256 + 16 * g);
-      q4s[4] = qsc[16 + g];
-    }
-  }
-  if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
   const float c_log2 = a.sm_scale_log2e * qs * ks;
   const float out_mul = KF == FFP8 ? ks : 1.0f;
   // Wait for the page ids and Q together, and make the compiler see Q as
@@ -762,60 +763,77 @@ void stage1_kernel(Stage1Args a) {
     }
   }
 
-  // ---- merge the four waves (log2-domain weights), then write
+  // ---- merge the four waves (log2-domain weights), then write.  Every wave
+  // parks its O^T fragments and (m, l) in LDS (the staging rings are idle
+  // now), then wave v merges fragments 8v..8v+7 -- a quarter of the output
+  // columns -- over the four waves and stores them, so one barrier separates
+  // the two halves and the output stores are spread over the waves.
   l_run = group_sum(l_run);
   __syncthreads();
   const int ob0 = static_cast<int>(smem0);
-  const int mlb = ob0 + 2 * 128 * 64 * 4;  // m[w][16], l[w][16]
-  auto put = [&](int buf) {
+  const int mlb = ob0 + kWaves * 32768;  // m[w][16], l[w][16]
 #pragma unroll
-    for (int c = 0; c < 32; ++c) lds_st<f32x4_t>(ob0 + buf * 32768 + (c * 64 + lane) * 16, acc[c]);
-    if (g == 0) {
-      lds_st<float>(mlb + (w * kHeads + hq) * 4, m_run);
-      lds_st<float>(mlb + (kWaves * kHeads + w * kHeads + hq) * 4, l_run);
-    }
-  };
-  auto merge = [&](int buf, int wp) {
-    const float ma = lds_ld<float>(mlb + (wp * kHeads + hq) * 4);
-    const float la = lds_ld<float>(mlb + (kWaves * kHeads + wp * kHeads + hq) * 4);
-    const float M = fmax3(ma, m_run);
-    const float fa = ma == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(ma - M);
-    const float fb = m_run == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  for (int c = 0; c < 32; ++c) lds_st<f32x4_t>(ob0 + w * 32768 + (c * 64 + lane) * 16, acc[c]);
+  if (g == 0) {
+    lds_st<float>(mlb + (w * kHeads + hq) * 4, m_run);
+    lds_st<float>(mlb + (kWaves * kHeads + w * kHeads + hq) * 4, l_run);
+  }
+  __syncthreads();
+  float mw[kWaves], lw[kWaves];
 #pragma unroll
-    for (int c = 0; c < 32; ++c) acc[c] = acc[c] * fb + lds_ld<f32x4_t>(ob0 + buf * 32768 + (c * 64 + lane) * 16) * fa;
-    l_run = l_run * fb + la * fa;
-    m_run = M;
-  };
-  if (w >= 2) put(w - 2);
-  __syncthreads();
-  if (w < 2) merge(w, w + 2);
-  __syncthreads();
-  if (w == 1) put(0);
-  __syncthreads();
-  if (w != 0) return;
-  merge(0, 1);
+  for (int v = 0; v < kWaves; ++v) {
+    mw[v] = lds_ld<float>(mlb + (v * kHeads + hq) * 4);
+    lw[v] = lds_ld<float>(mlb + (kWaves * kHeads + v * kHeads + hq) * 4);
+  }
+  f32x4_t part[kWaves][8];
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[v][i] = lds_ld<f32x4_t>(ob0 + v * 32768 + ((8 * w + i) * 64 + lane) * 16);
+  sched_fence();
+  float M = mw[0];
+#pragma unroll
+  for (int v = 1; v < kWaves; ++v) M = fmaxf(M, mw[v]);
+  float fv[kWaves];
+  float lsum = 0.0f;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    fv[v] = mw[v] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mw[v] - M);
+    lsum += lw[v] * fv[v];
+  }
+  f32x4_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    o[i] = part[0][i] * fv[0];
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) o[i] += part[v][i] * fv[v];
+  }
 
-  const bool nonempty = l_run > 0.0f;
-  const float mul = nonempty ? out_mul / l_run : 0.0f;
-  const float lse = nonempty ? m_run + __builtin_amdgcn_logf(l_run) : -__builtin_huge_valf();
+  const bool nonempty = lsum > 0.0f;
+  const float mul = nonempty ? out_mul / lsum : 0.0f;
+  const float lse = nonempty ? M + __builtin_amdgcn_logf(lsum) : -__builtin_huge_valf();
   const size_t orow = static_cast<size_t>(b) * kHeads + hq;
+  // fragment c = 8w + i; non-mxfp4 row r of fragment c is output column
+  // 16c + 4g + r, mxfp4 row r is column 32(4g + r) + c
   if (S == 1) {
     uint16_t* op = a.out + orow * kDv;
     if constexpr (KF == FMX) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-          const bf16x2_t p0 = {static_cast<__bf16>(acc[4 * c4 + 0][r] * mul), static_cast<__bf16>(acc[4 * c4 + 1][r] * mul)};
-          const bf16x2_t p1 = {static_cast<__bf16>(acc[4 * c4 + 2][r] * mul), static_cast<__bf16>(acc[4 * c4 + 3][r] * mul)};
-          *reinterpret_cast<i32x2_t*>(op + 32 * (4 * g + r) + 4 * c4) = i32x2_t{static_cast<int>(bits(p0)), static_cast<int>(bits(p1))};
+        for (int h4 = 0; h4 < 2; ++h4) {
+          const bf16x2_t p0 = {static_cast<__bf16>(o[4 * h4 + 0][r] * mul), static_cast<__bf16>(o[4 * h4 + 1][r] * mul)};
+          const bf16x2_t p1 = {static_cast<__bf16>(o[4 * h4 + 2][r] * mul), static_cast<__bf16>(o[4 * h4 + 3][r] * mul)};
+          *reinterpret_cast<i32x2_t*>(op + 32 * (4 * g + r) + 8 * w + 4 * h4) =
+              i32x2_t{static_cast<int>(bits(p0)), static_cast<int>(bits(p1))};
         }
     } else {
 #pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        const bf16x2_t p0 = {static_cast<__bf16>(acc[c][0] * mul), static_cast<__bf16>(acc[c][1] * mul)};
-        const bf16x2_t p1 = {static_cast<__bf16>(acc[c][2] * mul), static_cast<__bf16>(acc[c][3] * mul)};
-        *reinterpret_cast<i32x2_t*>(op + 16 * c + 4 * g) = i32x2_t{static_cast<int>(bits(p0)), static_cast<int>(bits(p1))};
+      for (int i = 0; i < 8; ++i) {
+        const bf16x2_t p0 = {static_cast<__bf16>(o[i][0] * mul), static_cast<__bf16>(o[i][1] * mul)};
+        const bf16x2_t p1 = {static_cast<__bf16>(o[i][2] * mul), static_cast<__bf16>(o[i][3] * mul)};
+        *reinterpret_cast<i32x2_t*>(op + 16 * (8 * w + i) + 4 * g) =
+            i32x2_t{static_cast<int>(bits(p0)), static_cast<int>(bits(p1))};
       }
     }
   } else {
@@ -825,14 +843,14 @@ void stage1_kernel(Stage1Args a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4)
-          *reinterpret_cast<f32x4_t*>(po + 32 * (4 * g + r) + 4 * c4) =
-              f32x4_t{acc[4 * c4][r], acc[4 * c4 + 1][r], acc[4 * c4 + 2][r], acc[4 * c4 + 3][r]} * mul;
+        for (int h4 = 0; h4 < 2; ++h4)
+          *reinterpret_cast<f32x4_t*>(po + 32 * (4 * g + r) + 8 * w + 4 * h4) =
+              f32x4_t{o[4 * h4][r], o[4 * h4 + 1][r], o[4 * h4 + 2][r], o[4 * h4 + 3][r]} * mul;
     } else {
 #pragma unroll
-      for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4_t*>(po + 16 * c + 4 * g) = acc[c] * mul;
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4_t*>(po + 16 * (8 * w + i) + 4 * g) = o[i] * mul;
     }
-    if (g == 0) a.part_lse[prow] = lse;
+    if (w == 0 && g == 0) a.part_lse[prow] = lse;
   }
 }
 

@@ -223,6 +223,45 @@ def test_deterministic_and_reseeded_buffers(orc):
     check_close(c, ref2, what="reseeded")
 
 
+@pytest.mark.parametrize("S", [1, 4])
+def test_graph_replay_matches_eager(orc, S):
+    """Decode captured in a HIP graph (how a serving loop issues it) gives the
+    eager result on every replay, with unrelated eager work in between."""
+    case = synth.make_case(3, [700, 45, 1200], 8, shuffle=True, seed=820)
+    g, o = prepare(case, "bf16", "fp8", orc)
+    eager = gpu_decode(case, g, S).clone()
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(eager, ref, what=f"eager S={S}")
+    out = torch.empty_like(eager)
+    ws_bytes = mla.workspace_bytes(3, S)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV) if ws_bytes else None
+
+    def call():
+        mla.decode(g["q"], g["kv"], g["kv_indptr"], g["page_table"], case["page_size"], S,
+                   kv_scale=g["kv_scale"], out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    other = synth.make_case(2, [300, 64], 8, shuffle=False, seed=821)
+    go, _ = prepare(other, "bf16", "fp8", orc)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        if ws is not None:
+            ws.fill_(0xFF)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+        gpu_decode(other, go, 2)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_empty_batch_is_noop():
     q = torch.empty((0, 16, 576), dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros((8, 576), dtype=torch.bfloat16, device=DEV)
