@@ -58,6 +58,9 @@ typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(8))) unsigned u32x8_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 typedef __attribute__((address_space(3))) char lds_char;
 
 // ------------------------------------------------------------------ layout
@@ -181,6 +184,68 @@ __device__ __forceinline__ float e8m0_f32(uint32_t e) {
 
 __device__ __forceinline__ uint32_t bits(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Exact two-term fp8 form of one lane's 32 bf16 values of a QK MFMA B
+// operand: x = hi * 2^(s-127) + lo * 2^(s'-127), s and s' the e8m0 scales of
+// x's scale block.  In the 8-bit operand of the 16x16x128 f8f6f4 MFMA, byte
+// half h (16 values) of lane group g belongs to scale block 2h + (g >> 1),
+// shared with the partner group g ^ 1, and lane group g supplies the scale of
+// block g.  hi carries the leading four significant bits of x (RNE to e4m3),
+// lo the rest: a bf16 significand has eight bits, so both terms are exact for
+// every element within 2^13 of its block maximum (both stay in the e4m3
+// normal range); smaller elements keep an absolute resolution of 2^-13 times
+// the block maximum.  The hi scale puts the block maximum in [128, 256).
+// raw[0..1] hold the 16 values of half 0, raw[2..3] those of half 1.
+__device__ __forceinline__ void split_q_fp8(const u32x4_t raw[4], int g, i32x8_t& hi, i32x8_t& lo, uint32_t& sh,
+                                            uint32_t& sl) {
+  float x[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * j + 2 * e] = __uint_as_float(raw[j][e] << 16);
+      x[8 * j + 2 * e + 1] = __uint_as_float(raw[j][e] & 0xffff0000u);
+    }
+  float am[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am[i >> 4] = fmaxf(am[i >> 4], fabsf(x[i]));
+  int eh[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float bm = fmaxf(am[h], __shfl_xor(am[h], 16));  // block max over the lane pair
+    eh[h] = max(static_cast<int>((__float_as_uint(bm) >> 23) & 0xffu) - 127 - 7, -127);
+  }
+  u32x8_t hv, lv;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int h = k >> 2;
+    const int el = max(eh[h] - 4, -127);
+    const float inv = __uint_as_float(static_cast<uint32_t>(127 - eh[h]) << 23);     // 2^-eh
+    const float up = __uint_as_float(static_cast<uint32_t>(127 + eh[h] - el) << 23);  // 2^(eh-el)
+    const float a0 = x[4 * k] * inv, a1 = x[4 * k + 1] * inv, a2 = x[4 * k + 2] * inv, a3 = x[4 * k + 3] * inv;
+    // the scalef32 converters use the OCP e4m3 encoding the f8f6f4 MFMA reads
+    i16x2_t ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, a0, a1, 1.0f, false);
+    ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(ph, a2, a3, 1.0f, true);
+    const int phi = __builtin_bit_cast(int, ph);
+    const f32x2_t d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(phi, 1.0f, false);
+    const f32x2_t d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(phi, 1.0f, true);
+    i16x2_t pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, (a0 - d01[0]) * up, (a1 - d01[1]) * up,
+                                                          1.0f, false);
+    pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, (a2 - d23[0]) * up, (a3 - d23[1]) * up, 1.0f, true);
+    hv[k] = static_cast<uint32_t>(phi);
+    lv[k] = __builtin_bit_cast(uint32_t, pl);
+  }
+  hi = __builtin_bit_cast(i32x8_t, hv);
+  lo = __builtin_bit_cast(i32x8_t, lv);
+  // lane group g supplies block g = (half g >> 1 of pair g & 1): groups 0 and 3
+  // hold it themselves, groups 1 and 2 swap
+  const int send = g == 2 ? eh[0] : eh[1];
+  const int ln = __lane_id();
+  const int got = __shfl(send, g == 1 ? ln + 16 : g == 2 ? ln - 16 : ln);
+  const int e_blk = g == 0 ? eh[0] : g == 3 ? eh[1] : got;
+  sh = static_cast<uint32_t>(e_blk + 127);
+  sl = static_cast<uint32_t>(max(e_blk - 4, -127) + 127);
+}
+
 // bf16 pair (lo = low half of x, hi = low half of y) and the same for high halves
 __device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return (x & 0xffffu) | (y << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xffff0000u); }
@@ -208,6 +273,11 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
 }
 __device__ __forceinline__ f32x4_t mfma_fp8(i32x8_t a, i32x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// e2m1 K with its block scales x fp8 Q with its block scales
+__device__ __forceinline__ f32x4_t mfma_fp4_fp8(i32x4_t a, uint32_t sa, i32x8_t b, uint32_t sb, f32x4_t c) {
+  i32x8_t A = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, b, c, 4, 0, 0, sa, 0, sb);
 }
 __device__ __forceinline__ f32x4_t mfma_fp4(i32x4_t a, uint32_t sa, i32x4_t b, uint32_t sb, f32x4_t c) {
   i32x8_t A = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
@@ -257,7 +327,7 @@ struct Stage1Args {
 template <int QF, int KF> struct QFrag;
 template <> struct QFrag<FBF16, FBF16> { static constexpr int kN = 18; };
 template <> struct QFrag<FBF16, FFP8> { static constexpr int kN = 18; };
-template <> struct QFrag<FBF16, FMX> { static constexpr int kN = 18; };
+template <> struct QFrag<FBF16, FMX> { static constexpr int kN = 5; };  // hi/lo fp8 pairs
 template <> struct QFrag<FFP8, FFP8> { static constexpr int kN = 5; };
 template <> struct QFrag<FMX, FMX> { static constexpr int kN = 5; };
 
@@ -294,12 +364,35 @@ void stage1_kernel(Stage1Args a) {
   // depend on the request index only, so their latency overlaps the
   // kv_indptr load and the page-id gathers that follow.
   constexpr int NQ = QFrag<QF, KF>::kN;
-  bf16x8_t qb[QF == FBF16 ? NQ : 1];
-  i32x8_t q8[QF == FFP8 ? NQ : 1];
+  // bf16 Q over the mxfp4 cache runs QK on the scaled f8f6f4 MFMA with Q as
+  // an exact hi + lo pair of fp8 operands (split_q_fp8), so the e2m1 K needs
+  // no conversion; raw bf16 blocks are held until the loads have landed.  The
+  // split costs a few microseconds per wave (the fp8 encoder is a slow
+  // instruction), which only the long, compute-bound mxfp4 splits repay; over
+  // the fp8 cache, K is widened to bf16 instead (full-rate converts).
+  constexpr bool kSplitQ = QF == FBF16 && KF == FMX;
+  bf16x8_t qb[QF == FBF16 && !kSplitQ ? NQ : 1];
+  u32x4_t qraw[kSplitQ ? 4 * NQ : 1];
+  i32x8_t q8[QF == FFP8 || kSplitQ ? NQ : 1];
+  i32x8_t ql[kSplitQ ? NQ : 1];
+  uint32_t qhs[kSplitQ ? NQ : 1], qls[kSplitQ ? NQ : 1];
   i32x4_t q4[QF == FMX ? NQ : 1];
   uint32_t q4s[QF == FMX ? NQ : 1];
   float qs = 1.0f, ks = 1.0f;
-  if constexpr (QF == FBF16) {
+  if constexpr (kSplitQ) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // the 4-bit K operand is contiguous per lane group (dims 128c + 32g +
+        // [0, 32)), the 8-bit one puts byte half h of lane group g at K
+        // position 64h + 16g: half h = j >> 1 takes dims 128c + 64h + 16g + [0, 16)
+        const int d = 128 * c + 64 * (j >> 1) + 16 * g + 8 * (j & 1);
+        qraw[4 * c + j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (d < kDqk) qraw[4 * c + j] = *reinterpret_cast<const u32x4_t*>(qrow + d);
+      }
+  } else if constexpr (QF == FBF16) {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
 #pragma unroll
     for (int m = 0; m < NQ; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qrow + qdim_bf16<KF>(m, g));
@@ -437,7 +530,12 @@ void stage1_kernel(Stage1Args a) {
   // Wait for the page ids and Q together, and make the compiler see Q as
   // complete here, so its own wait for Q cannot drain the in-flight tiles later.
   wait_vm<0>();
-  if constexpr (QF == FBF16) {
+  if constexpr (kSplitQ) {
+    // split after the first tile DMAs are issued (below): it then overlaps
+    // their latency instead of delaying them
+#pragma unroll
+    for (int i = 0; i < 4 * NQ; ++i) asm volatile("" : "+v"(qraw[i]));
+  } else if constexpr (QF == FBF16) {
 #pragma unroll
     for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(qb[m]));
   } else if constexpr (QF == FFP8) {
@@ -544,43 +642,7 @@ void stage1_kernel(Stage1Args a) {
       const int pr = static_cast<int>(par_addr(x));
       const int sb0 = static_cast<int>(sc_addr(x)) + 20 * tq0 + 2 * lds_ld<uint8_t>(pr + tq0);
       const int sb1 = static_cast<int>(sc_addr(x)) + 20 * tq1 + 2 * lds_ld<uint8_t>(pr + tq1);
-      if constexpr (QF == FBF16) {
-        i32x4_t u0[4], u1[4];
-        uint32_t r0[2], r1[2], c0[6], c1[6];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          u0[c] = lds_ld<i32x4_t>(qoff(tq0, c));
-          u1[c] = lds_ld<i32x4_t>(qoff(tq1, c));
-          c0[c] = lds_ld<uint8_t>(sb0 + 4 * c + g);
-          c1[c] = lds_ld<uint8_t>(sb1 + 4 * c + g);
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          r0[e] = lds_ld<uint32_t>(tb + 16 * (tq0 * U + 16 + e) + 4 * g);
-          r1[e] = lds_ld<uint32_t>(tb + 16 * (tq1 * U + 16 + e) + 4 * g);
-          c0[4 + e] = lds_ld<uint8_t>(sb0 + 16 + e);
-          c1[4 + e] = lds_ld<uint8_t>(sb1 + 16 + e);
-        }
-        sched_fence();
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          pin2(u0[c], u1[c]);
-          const float f0 = e8m0_f32(c0[c]), f1 = e8m0_f32(c1[c]);
-          s0 = mfma_bf16(cvt_fp4x8(u0[c].x, f0), qb[4 * c + 0], s0);
-          s1 = mfma_bf16(cvt_fp4x8(u1[c].x, f1), qb[4 * c + 0], s1);
-          s0 = mfma_bf16(cvt_fp4x8(u0[c].y, f0), qb[4 * c + 1], s0);
-          s1 = mfma_bf16(cvt_fp4x8(u1[c].y, f1), qb[4 * c + 1], s1);
-          s0 = mfma_bf16(cvt_fp4x8(u0[c].z, f0), qb[4 * c + 2], s0);
-          s1 = mfma_bf16(cvt_fp4x8(u1[c].z, f1), qb[4 * c + 2], s1);
-          s0 = mfma_bf16(cvt_fp4x8(u0[c].w, f0), qb[4 * c + 3], s0);
-          s1 = mfma_bf16(cvt_fp4x8(u1[c].w, f1), qb[4 * c + 3], s1);
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          s0 = mfma_bf16(cvt_fp4x8(r0[e], e8m0_f32(c0[4 + e])), qb[16 + e], s0);
-          s1 = mfma_bf16(cvt_fp4x8(r1[e], e8m0_f32(c1[4 + e])), qb[16 + e], s1);
-        }
-      } else {
+      {
         i32x4_t u0[5], u1[5];
         uint32_t c0[5], c1[5];
 #pragma unroll
@@ -601,11 +663,25 @@ void stage1_kernel(Stage1Args a) {
           c1[4] = lds_ld<uint8_t>(sb1 + 16 + g);
         }
         sched_fence();
+        if constexpr (kSplitQ) {
+          f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 5; ++c) {
-          pin2(u0[c], u1[c]);
-          s0 = mfma_fp4(u0[c], c0[c], q4[c], q4s[c], s0);
-          s1 = mfma_fp4(u1[c], c1[c], q4[c], q4s[c], s1);
+          for (int c = 0; c < 5; ++c) {
+            pin2(u0[c], u1[c]);
+            s0 = mfma_fp4_fp8(u0[c], c0[c], q8[c], qhs[c], s0);
+            s1 = mfma_fp4_fp8(u1[c], c1[c], q8[c], qhs[c], s1);
+            t0 = mfma_fp4_fp8(u0[c], c0[c], ql[c], qls[c], t0);
+            t1 = mfma_fp4_fp8(u1[c], c1[c], ql[c], qls[c], t1);
+          }
+          s0 += t0;
+          s1 += t1;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 5; ++c) {
+            pin2(u0[c], u1[c]);
+            s0 = mfma_fp4(u0[c], c0[c], q4[c], q4s[c], s0);
+            s1 = mfma_fp4(u1[c], c1[c], q4[c], q4s[c], s1);
+          }
         }
       }
     }
@@ -739,6 +815,10 @@ void stage1_kernel(Stage1Args a) {
       if (X >= D) wait_vm<D * NDMA + D - 1>();
       issue_pid(X + D);
       issue_tile(X);
+    }
+    if constexpr (kSplitQ) {
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) split_q_fp8(qraw + 4 * c, g, q8[c], ql[c], qhs[c], qls[c]);
     }
     for (int jx = 0; jx < nloc; ++jx) {
       const int ahead = min(nloc - 1, jx + NBUF - 1) - jx;

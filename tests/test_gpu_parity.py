@@ -223,6 +223,27 @@ def test_deterministic_and_reseeded_buffers(orc):
     check_close(c, ref2, what="reseeded")
 
 
+@pytest.mark.parametrize("qf,kf", PAIRS)
+def test_block_scaled_inputs(orc, qf, kf):
+    """Every 32-dim block of every Q and cache row scaled by its own power of
+    two in [2^-6, 2^6]: the mxfp4 e8m0 block scales (and the MFMA scale lanes
+    that apply them) then differ block to block, which N(0,1) rows do not
+    exercise.  Q is damped so the logits stay O(1)."""
+    case = synth.make_case(3, [300, 97, 640], 8, shuffle=True, seed=830)
+    gen = torch.Generator().manual_seed(831)
+    kexp = torch.randint(-6, 7, (case["kv"].shape[0], 18), generator=gen).to(torch.float32)
+    qexp = torch.randint(-6, 7, (3, 16, 18), generator=gen).to(torch.float32)
+    kv = case["kv"].to(torch.float32).view(-1, 18, 32) * torch.exp2(kexp)[..., None]
+    q = case["q"].to(torch.float32).view(3, 16, 18, 32) * torch.exp2(qexp - 8)[..., None]
+    case["kv"] = kv.view(-1, 576).to(torch.bfloat16)
+    case["q"] = q.view(3, 16, 576).to(torch.bfloat16)
+    g, o = prepare(case, qf, kf, orc, q_static=float(case["q"].abs().max()) / 448.0)
+    out = gpu_decode(case, g, 2)
+    ref, _ = oracle_decode(case, o, orc)
+    scale = max(1.0, float(np.abs(ref).max()))
+    check_close(out, ref, atol=2e-2 * scale, rtol=2e-2, what=f"block-scaled {qf}/{kf}")
+
+
 @pytest.mark.parametrize("S", [1, 4])
 def test_graph_replay_matches_eager(orc, S):
     """Decode captured in a HIP graph (how a serving loop issues it) gives the
