@@ -246,9 +246,11 @@ __device__ __forceinline__ void split_q_fp8(const u32x4_t raw[4], int g, i32x8_t
   sl = static_cast<uint32_t>(max(e_blk - 4, -127) + 127);
 }
 
-// bf16 pair (lo = low half of x, hi = low half of y) and the same for high halves
-__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return (x & 0xffffu) | (y << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xffff0000u); }
+// bf16 pair (lo = low half of x, hi = low half of y) and the same for high
+// halves: one byte permute each (v_perm_b32 indexes bytes 0-3 of its second
+// operand and 4-7 of its first)
+__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
 
 __device__ __forceinline__ bf16x8_t cvt_fp8x8(i32x2_t v) {
   u32x4_t r;
@@ -937,7 +939,10 @@ void stage1_kernel(Stage1Args a) {
 // ------------------------------------------------------------------ stage 2
 // One workgroup per (request, group of 4 heads); a thread merges 8 columns of
 // one head over the S splits with base-2 log-sum-exp weights (empty splits,
-// LSE = -inf, are skipped; an all-empty request yields zeros).
+// LSE = -inf, are skipped; an all-empty request yields zeros).  One pass: the
+// LSEs and partial rows of eight splits are loaded together, and the running
+// maximum moves with a rescale of the accumulator (one load round trip for
+// S <= 8).
 __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
                                                      uint16_t* __restrict__ out, int S) {
   const int b = blockIdx.x >> 2;
@@ -946,47 +951,39 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
   const float* lse = part_lse + static_cast<size_t>(b) * S * kHeads + hq;
   const float* po = part_o + (static_cast<size_t>(b) * S * kHeads + hq) * kDv + col;
   constexpr float kNegInf = -__builtin_huge_valf();
-  // pass 1: the largest split LSE, eight independent loads in flight per step
-  float M = kNegInf;
-  int s = 0;
-  for (; s + 8 <= S; s += 8) {
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = lse[(s + i) * kHeads];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) M = fmax3(M, v[i]);
-  }
-  for (; s < S; ++s) M = fmax3(M, lse[s * kHeads]);
-  // pass 2: weighted sum, four splits (eight 16-byte loads) in flight per step;
-  // an empty split (LSE = -inf) gets weight 0
+  constexpr int kB = 8;
+  float M = kNegInf, ws = 0.0f;
   f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  float ws = 0.0f;
-  if (M != kNegInf) {
-    s = 0;
-    for (; s + 4 <= S; s += 4) {
-      float l[4];
-      f32x4_t x0[4], x1[4];
+  for (int s0 = 0; s0 < S; s0 += kB) {
+    float l[kB];
+    f32x4_t x0[kB], x1[kB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        l[i] = lse[(s + i) * kHeads];
-        x0[i] = *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(s + i) * kHeads * kDv);
-        x1[i] = *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(s + i) * kHeads * kDv + 4);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float wgt = l[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l[i] - M);
-        a0 += x0[i] * wgt;
-        a1 += x1[i] * wgt;
-        ws += wgt;
-      }
+    for (int i = 0; i < kB; ++i) {
+      const int si = min(s0 + i, S - 1);  // past the end: a repeat, weighted 0 below
+      l[i] = lse[si * kHeads];
+      x0[i] = *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(si) * kHeads * kDv);
+      x1[i] = *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(si) * kHeads * kDv + 4);
     }
-    for (; s < S; ++s) {
-      const float l = lse[s * kHeads];
-      const float wgt = l == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l - M);
-      a0 += *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(s) * kHeads * kDv) * wgt;
-      a1 += *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(s) * kHeads * kDv + 4) * wgt;
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      if (s0 + i >= S) l[i] = kNegInf;
+    float mb = l[0];
+#pragma unroll
+    for (int i = 1; i < kB; ++i) mb = fmax3(mb, l[i]);
+    if (mb == kNegInf) continue;  // every split of this batch is empty
+    const float Mn = fmax3(M, mb);
+    const float r = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    a0 *= r;
+    a1 *= r;
+    ws *= r;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const float wgt = l[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l[i] - Mn);
+      a0 += x0[i] * wgt;
+      a1 += x1[i] * wgt;
       ws += wgt;
     }
+    M = Mn;
   }
   const float inv = ws > 0.0f ? 1.0f / ws : 0.0f;
   a0 *= inv;
