@@ -453,7 +453,7 @@ void stage1_kernel(Stage1Args a) {
   // unit): the row-pointer table offset and the byte offset inside the row.
   // Formats with up to 18 instructions per sub-tile keep these in registers;
   // bf16 (36) recomputes them from an opaque lane index instead.
-  constexpr bool kPre = Kv<KF>::kNdmaX4 <= 18;
+  constexpr bool kPre = Kv<KF>::kNdmaX4 <= 36;
   auto dma_pack = [](int i, int ln) {
     const int c = 64 * i + ln;
     const int t = c / U;
@@ -560,6 +560,8 @@ void stage1_kernel(Stage1Args a) {
   // P*V token slots of this lane group: slot kk <-> token (kk<4 ? 4g+kk : 16+4g+kk-4)
   auto compute = [&](int x, int ntok) {
     const int tb = static_cast<int>(slot_addr(x));
+#pragma unroll
+    for (int c = 0; c < 32; c += 8) pin_acc8(acc + c);
     // fp8 V^T fragments for P*V, one transposing read per 16-column tile:
     // lane j of a 16-lane group addresses token T[j/2] (8 B at column 8*(j%2)),
     // T = {4g..4g+3, 16+4g..16+4g+3}; lane i then holds column i of all eight.
@@ -687,6 +689,9 @@ void stage1_kernel(Stage1Args a) {
         }
       }
     }
+    // the logits are consumed by VALU code: keep them out of the AGPRs that
+    // hold the O accumulator
+    asm volatile("" : "+v"(s0), "+v"(s1));
     // ---------------- online softmax (log2 domain); lane holds head hq,
     // tokens 4g+r (tile 0) and 16+4g+r (tile 1).  The reference max is only
     // moved when a logit exceeds it by more than 2^kLazy, so the O rescale
