@@ -126,11 +126,15 @@ size_t mla_workspace_bytes(int32_t batch, int32_t num_splits);
 /*
  * mla_choose_num_splits - split count for `batch` requests of about
  * `kv_len` tokens on a device with `num_cus` compute units (0 = 256, MI355X).
- * Occupancy model: aim for batch*S close to a whole number of waves of
- * one-workgroup-per-CU, keep at least 256 tokens per split, and keep the
- * stage-2 partial traffic small; see the design notes for the calibration.
- * (Page 695854's split selectors and page 668813's split tables pick S per
- * shape for the same reasons.)  Returns a value in 1..MLA_MAX_SPLITS.
+ * On the tuned grid (batch 4/32/64/256 x kv_len 1024/8192 x each cache
+ * format, MI355X) it returns the measured fastest S, from a table written by
+ * mla_latent_kv_13_amd/tune_splits.py.  Elsewhere an occupancy cost model
+ * decides: ceil(batch*S / num_cus) rounds of one workgroup per CU, each
+ * streaming its chunk rounded up to 128 tokens, plus for S > 1 the partial
+ * outputs, a second launch and a per-split stage-2 latency; the model alone
+ * reproduces every tuned optimum of the grid.  (Page 695854's split selectors
+ * and page 668813's split tables pick S per shape for the same reasons.)
+ * Returns a value in 1..MLA_MAX_SPLITS; pure host code.
  */
 int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, int32_t num_cus);
 

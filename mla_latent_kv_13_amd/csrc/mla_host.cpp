@@ -29,6 +29,18 @@ int64_t kv_row_bytes(int32_t kd) {
 
 }  // namespace
 
+namespace {
+// Measured fastest split counts on the 8-shape grid, written by
+// mla_latent_kv_13_amd/tune_splits.py.
+struct SplitEntry {
+  int32_t batch, kv_len, kv_dtype, splits;
+  double us;
+};
+constexpr SplitEntry kSplitTable[] = {
+#include "split_table.inc"
+};
+}  // namespace
+
 extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
@@ -87,13 +99,23 @@ int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, i
   if (batch < 1 || kv_len < 1) return 1;
   if (num_cus <= 0) num_cus = 256;
   if (kv_dtype < MLA_DTYPE_BF16 || kv_dtype > MLA_DTYPE_MXFP4) kv_dtype = MLA_DTYPE_FP8_E4M3FN;
+  // Shapes of the tuned grid (MI355X, 256 CUs) take the measured optimum.
+  if (num_cus == 256) {
+    for (const SplitEntry& e : kSplitTable)
+      if (e.batch == batch && e.kv_len == kv_len && e.kv_dtype == kv_dtype) return e.splits;
+  }
   // Cost in "bytes streamed by the busiest CU": stage 1 runs in
   // ceil(batch*S / num_cus) rounds of one workgroup per CU, each streaming
   // its chunk rounded up to 128 tokens (four waves x 32-token sub-tiles);
   // S > 1 adds the partial outputs (written and re-read, spread over the
-  // CUs) and a fixed second launch worth ~3 us of per-CU bandwidth.
-  const double row = static_cast<double>(kv_row_bytes(kv_dtype));
-  const double launch_bytes = 3.0e-6 * 8.0e12 / 256.0;
+  // CUs), a fixed second launch worth ~3 us of per-CU bandwidth, and ~0.12 us
+  // of stage-2 latency per split (its split loop), as measured on the grid.
+  // mxfp4 tiles take as long to compute as fp8 ones (the e2m1 -> bf16 work
+  // for P*V), so they are priced like a 576-byte fp8 row, not by their bytes
+  const double row = static_cast<double>(kv_dtype == MLA_DTYPE_MXFP4 ? MLA_HEAD_DIM_QK : kv_row_bytes(kv_dtype));
+  const double cu_bytes_per_us = 8.0e12 / 256.0 * 1e-6;
+  const double launch_bytes = 3.0 * cu_bytes_per_us;
+  const double per_split_bytes = 0.12 * cu_bytes_per_us;
   const int32_t max_s = kv_len / 32 < 1 ? 1 : (kv_len / 32 > MLA_MAX_SPLITS ? MLA_MAX_SPLITS : kv_len / 32);
   double best = 0.0;
   int32_t best_s = 1;
@@ -104,7 +126,7 @@ int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, i
     double cost = static_cast<double>(rounds) * static_cast<double>(chunk_eff) * row;
     if (s > 1) {
       const double partial = static_cast<double>(batch) * s * MLA_NUM_HEADS * (MLA_HEAD_DIM_V + 1) * 4.0 * 2.0;
-      cost += partial / num_cus + launch_bytes;
+      cost += partial / num_cus + launch_bytes + per_split_bytes * s;
     }
     if (s == 1 || cost < best * 0.999) {
       best = cost;

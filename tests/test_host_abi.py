@@ -107,6 +107,26 @@ def test_split_heuristic(lib):
     assert mla.choose_num_splits(32, 1024, mla.FP8) >= 4
 
 
+def split_table():
+    path = os.path.join(os.path.dirname(os.path.dirname(__file__)), "mla_latent_kv_13_amd", "csrc", "split_table.inc")
+    rows = []
+    for line in open(path):
+        m = re.match(r"\{(\d+), (\d+), (\d+), (\d+), ([0-9.]+)\}", line.strip())
+        if m:
+            rows.append(tuple(int(x) for x in m.groups()[:4]))
+    return rows
+
+
+def test_split_table_is_used_and_matched_by_the_model(lib):
+    rows = split_table()
+    assert len(rows) == 24  # 4 batches x 2 lengths x 3 cache formats
+    for batch, kv_len, kd, s in rows:
+        assert mla.choose_num_splits(batch, kv_len, kd) == s
+        # the cost model alone (another CU count bypasses the MI355X table)
+        # reproduces every tuned optimum of the grid
+        assert mla.choose_num_splits(batch, kv_len, kd, 257) == s, (batch, kv_len, kd)
+
+
 def test_stream_read_argument_errors(lib):
     # every one of these is rejected (or is a no-op) before anything is launched
     assert lib.mla_stream_read(A, 0, A2, None) == 0
