@@ -89,8 +89,11 @@ def build_inputs(w, device):
         ops["kv"], ops["kv_scale"] = mla.quantize_mxfp4(case["kv"])
     else:
         ops["kv"], ops["kv_scale"] = case["kv"], None
+    if w.q_fmt != "bf16":
+        ops["q_bf16"] = case["q"]  # kept for the timing that includes the Q quantiser
     if w.q_fmt == "fp8":
-        ops["q"], ops["q_scale"] = mla.quantize_fp8(case["q"], w.q_scale)
+        ops["q_scale_static"] = torch.tensor([w.q_scale], dtype=torch.float32, device=device)
+        ops["q"], ops["q_scale"] = mla.quantize_fp8(case["q"], ops["q_scale_static"])
     elif w.q_fmt == "mxfp4":
         p, s = mla.quantize_mxfp4(case["q"].reshape(B * 16, 576))
         ops["q"], ops["q_scale"] = p.reshape(B, 16, 288), s
@@ -190,6 +193,18 @@ def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
         "partial_bytes": 2 * mla.workspace_bytes(w.batch, S),
         "tflops": round(FLOPS_PER_TOKEN * w.batch * w.kv_len / (ev_ms * 1e-3) / 1e12, 2),
     }
+    if extras and w.q_fmt != "bf16":
+        # end to end from bf16 Q: the Q quantiser (one launch) plus the decode
+        def call_q(i):
+            r = reps[i % nrep]
+            if w.q_fmt == "fp8":
+                mla.quantize_fp8(r["q_bf16"], r["q_scale_static"], out=r["q"])
+            else:
+                mla.quantize_mxfp4(r["q_bf16"].view(w.batch * 16, 576),
+                                   out=(r["q"].view(w.batch * 16, 288), r["q_scale"]))
+            mla.decode(r["q"], r["kv"], r["kv_indptr"], r["page_table"], w.page_size, S, q_scale=r["q_scale"],
+                       kv_scale=r["kv_scale"], out=r["out"], workspace=r["ws"])
+        res["us_with_q_quant"] = round(time_calls(call_q, steps, warmup, 0.05, per_graph)[0] * 1e3, 3)
     if extras and nrep > 1:
         warm = time_calls(caller(S, 1), steps, warmup, 0.05, min(nrep, 64))[0]
         res["us_warm_same_buffers"] = round(warm * 1e3, 3)

@@ -176,11 +176,12 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
     return out
 
 
-def quantize_fp8(x: torch.Tensor, scale: torch.Tensor | float | None = None, stream=None):
+def quantize_fp8(x: torch.Tensor, scale: torch.Tensor | float | None = None, stream=None, out=None):
     """Per-tensor OCP e4m3fn quantisation of a bf16 tensor on the device.
 
     scale None -> dynamic (max|x| / 448, computed on the device); a float or a
-    1-element float32 device tensor -> static.  Returns (codes, scale_tensor).
+    1-element float32 device tensor -> static.  out: optional preallocated
+    float8_e4m3fn tensor of x's shape.  Returns (codes, scale_tensor).
     """
     _dev(x)
     if x.dtype != torch.bfloat16:
@@ -192,7 +193,10 @@ def quantize_fp8(x: torch.Tensor, scale: torch.Tensor | float | None = None, str
         sc = scale.to(device=x.device, dtype=torch.float32).reshape(1).contiguous()
     else:
         sc = torch.tensor([float(scale)], dtype=torch.float32, device=x.device)
-    codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device) if out is None else out
+    if codes.shape != x.shape or codes.dtype != torch.float8_e4m3fn:
+        raise ValueError("out must be a float8_e4m3fn tensor of the input's shape")
+    _dev(codes)
     rc = load().mla_quantize_fp8(x.data_ptr(), x.numel(), codes.data_ptr(), sc.data_ptr(), int(dynamic),
                                  _stream(stream))
     if rc:
@@ -207,21 +211,29 @@ def mxfp4_scale_buffer(rows: int, device) -> torch.Tensor:
     return base[:n].view(rows, MXFP4_ROW_SCALES)
 
 
-def quantize_mxfp4(x: torch.Tensor, stream=None):
+def quantize_mxfp4(x: torch.Tensor, stream=None, out=None):
     """OCP MX mxfp4 quantisation of a bf16 tensor [..., cols] (cols % 32 == 0).
 
     Returns (packed uint8 [..., cols/2], e8m0 uint8 [..., cols/32]); for 576-wide
-    rows the scale array's allocation is padded as mla_decode requires.
+    rows the scale array's allocation is padded as mla_decode requires.  out:
+    optional preallocated (packed, scales) pair of those shapes.
     """
     _dev(x)
     if x.dtype != torch.bfloat16:
         raise TypeError("quantize_mxfp4 expects bfloat16 input")
     cols = x.shape[-1]
     rows = x.numel() // cols if cols else 0
-    packed = torch.empty(x.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=x.device)
-    nsc = rows * (cols // 32)
-    base = torch.empty(max(16, ((nsc + 15) // 16) * 16), dtype=torch.uint8, device=x.device)
-    scales = base[:nsc].view(x.shape[:-1] + (cols // 32,))
+    if out is None:
+        packed = torch.empty(x.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=x.device)
+        nsc = rows * (cols // 32)
+        base = torch.empty(max(16, ((nsc + 15) // 16) * 16), dtype=torch.uint8, device=x.device)
+        scales = base[:nsc].view(x.shape[:-1] + (cols // 32,))
+    else:
+        packed, scales = out
+        if (packed.shape != x.shape[:-1] + (cols // 2,) or scales.shape != x.shape[:-1] + (cols // 32,)
+                or packed.dtype != torch.uint8 or scales.dtype != torch.uint8):
+            raise ValueError("out must be uint8 (packed [..., cols/2], scales [..., cols/32])")
+        _dev(packed, scales)
     rc = load().mla_quantize_mxfp4(x.data_ptr(), rows, cols, packed.data_ptr(), scales.data_ptr(), _stream(stream))
     if rc:
         raise StatusError("mla_quantize_mxfp4", rc)

@@ -33,6 +33,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 #include <utility>
 
 #include "mla_decode.h"
@@ -462,7 +463,28 @@ void stage1_kernel(Stage1Args a) {
   int dmao[kPre ? Kv<KF>::kNdmaX4 : 1];
 #pragma unroll
   for (int i = 0; i < (kPre ? Kv<KF>::kNdmaX4 : 1); ++i) dmao[i] = dma_pack(i, lane);
-  auto issue_tile = [&](int X) {
+  // With two slots per wave (fp8), a tile's DMAs are issued in three parts:
+  // the first KA right after the slot is freed, the rest interleaved with the
+  // next sub-tile's compute.  The address unit accepts a 1 KB direct-to-LDS
+  // load about every 16 clocks per CU, so a burst of 18 per wave (x4 waves)
+  // would hold the wave at issue for most of a microsecond.
+  constexpr bool kSplitDma = NBUF == 2;
+  constexpr int KA = kSplitDma ? 6 : Kv<KF>::kNdmaX4;
+  constexpr int KB = kSplitDma ? KA + (Kv<KF>::kNdmaX4 - KA) / 2 : Kv<KF>::kNdmaX4;
+  // DMAs [I0, I1) of tile X (row-pointer table already written)
+  auto issue_part = [&](int X, auto i0c, auto i1c) {
+    constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
+    if constexpr (I1 > I0) {
+      const int pt = static_cast<int>(wbase + L::kPtrOff);
+      uint64_t rptr[I1 - I0];
+#pragma unroll
+      for (int i = I0; i < I1; ++i) rptr[i - I0] = lds_ld<uint64_t>(pt + (dmao[i] >> 16));
+#pragma unroll
+      for (int i = I0; i < I1; ++i)
+        dma_x4_nt(reinterpret_cast<const char*>(rptr[i - I0]) + (dmao[i] & 0xffff), slot_addr(X % NBUF) + 1024u * i);
+    }
+  };
+  auto issue_tile = [&](int X, bool full) {
     const int x = X % NBUF;
     wait_lgkm0();  // every LDS read of the slot being refilled has completed
     const int ub = kSub * (w + kWaves * X);
@@ -487,6 +509,14 @@ void stage1_kernel(Stage1Args a) {
     int lnv = lane;
     if constexpr (!kPre) asm volatile("" : "+v"(lnv));
     auto issue_x4 = [&](int x) {
+      if constexpr (kSplitDma) {
+        if (full) {
+          issue_part(X, std::integral_constant<int, 0>(), std::integral_constant<int, Kv<KF>::kNdmaX4>());
+        } else {
+          issue_part(X, std::integral_constant<int, 0>(), std::integral_constant<int, KA>());
+        }
+        return;
+      }
 #pragma unroll
       for (int i0 = 0; i0 < Kv<KF>::kNdmaX4; i0 += NB) {
         uint64_t rptr[NB];
@@ -558,7 +588,8 @@ void stage1_kernel(Stage1Args a) {
   // Lane-constant LDS offsets used by the reads.
   const int tq0 = hq, tq1 = 16 + hq;  // QK A-operand rows: tokens of tile 0 / 1
   // P*V token slots of this lane group: slot kk <-> token (kk<4 ? 4g+kk : 16+4g+kk-4)
-  auto compute = [&](int x, int ntok) {
+  // pend: tile whose DMAs [KA, 18) are still to be issued (split mode), or -1
+  auto compute = [&](int x, int ntok, int pend) {
     const int tb = static_cast<int>(slot_addr(x));
 #pragma unroll
     for (int c = 0; c < 32; c += 8) pin_acc8(acc + c);
@@ -585,6 +616,10 @@ void stage1_kernel(Stage1Args a) {
     // ---------------- QK^T: both 16-token tiles at once (two independent
     // accumulator chains), every LDS fragment fetched before the MFMAs run.
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // A dependent MFMA waits for its predecessor's result, so the K
+    // dimension is spread over independent partial accumulators (four or
+    // more chains in flight) that are summed once at the end.
+    f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KF == FBF16) {
 #pragma unroll
       for (int hh2 = 0; hh2 < 2; ++hh2) {
@@ -598,8 +633,13 @@ void stage1_kernel(Stage1Args a) {
 #pragma unroll
         for (int i = 0; i < 9; ++i) {
           pin2(k0[i], k1[i]);
-          s0 = mfma_bf16(k0[i], qb[9 * hh2 + i], s0);
-          s1 = mfma_bf16(k1[i], qb[9 * hh2 + i], s1);
+          if (i & 1) {
+            t0 = mfma_bf16(k0[i], qb[9 * hh2 + i], t0);
+            t1 = mfma_bf16(k1[i], qb[9 * hh2 + i], t1);
+          } else {
+            s0 = mfma_bf16(k0[i], qb[9 * hh2 + i], s0);
+            s1 = mfma_bf16(k1[i], qb[9 * hh2 + i], s1);
+          }
         }
       }
     } else if constexpr (KF == FFP8 && QF == FBF16) {
@@ -615,8 +655,8 @@ void stage1_kernel(Stage1Args a) {
         pin2(k0[c], k1[c]);
         s0 = mfma_bf16(cvt_fp8x8(i32x2_t{k0[c].x, k0[c].y}), qb[2 * c], s0);
         s1 = mfma_bf16(cvt_fp8x8(i32x2_t{k1[c].x, k1[c].y}), qb[2 * c], s1);
-        s0 = mfma_bf16(cvt_fp8x8(i32x2_t{k0[c].z, k0[c].w}), qb[2 * c + 1], s0);
-        s1 = mfma_bf16(cvt_fp8x8(i32x2_t{k1[c].z, k1[c].w}), qb[2 * c + 1], s1);
+        t0 = mfma_bf16(cvt_fp8x8(i32x2_t{k0[c].z, k0[c].w}), qb[2 * c + 1], t0);
+        t1 = mfma_bf16(cvt_fp8x8(i32x2_t{k1[c].z, k1[c].w}), qb[2 * c + 1], t1);
       }
     } else if constexpr (KF == FFP8) {  // fp8 x fp8
       i32x8_t a0[5], a1[5];
@@ -639,8 +679,13 @@ void stage1_kernel(Stage1Args a) {
 #pragma unroll
       for (int c = 0; c < 5; ++c) {
         pin2(a0[c], a1[c]);
-        s0 = mfma_fp8(a0[c], q8[c], s0);
-        s1 = mfma_fp8(a1[c], q8[c], s1);
+        if (c & 1) {
+          t0 = mfma_fp8(a0[c], q8[c], t0);
+          t1 = mfma_fp8(a1[c], q8[c], t1);
+        } else {
+          s0 = mfma_fp8(a0[c], q8[c], s0);
+          s1 = mfma_fp8(a1[c], q8[c], s1);
+        }
       }
     } else {  // mxfp4 K: block scales read once per (token, block)
       const int pr = static_cast<int>(par_addr(x));
@@ -668,7 +713,6 @@ void stage1_kernel(Stage1Args a) {
         }
         sched_fence();
         if constexpr (kSplitQ) {
-          f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < 5; ++c) {
             pin2(u0[c], u1[c]);
@@ -677,18 +721,26 @@ void stage1_kernel(Stage1Args a) {
             t0 = mfma_fp4_fp8(u0[c], c0[c], ql[c], qls[c], t0);
             t1 = mfma_fp4_fp8(u1[c], c1[c], ql[c], qls[c], t1);
           }
-          s0 += t0;
-          s1 += t1;
         } else {
 #pragma unroll
           for (int c = 0; c < 5; ++c) {
             pin2(u0[c], u1[c]);
-            s0 = mfma_fp4(u0[c], c0[c], q4[c], q4s[c], s0);
-            s1 = mfma_fp4(u1[c], c1[c], q4[c], q4s[c], s1);
+            if (c & 1) {
+              t0 = mfma_fp4(u0[c], c0[c], q4[c], q4s[c], t0);
+              t1 = mfma_fp4(u1[c], c1[c], q4[c], q4s[c], t1);
+            } else {
+              s0 = mfma_fp4(u0[c], c0[c], q4[c], q4s[c], s0);
+              s1 = mfma_fp4(u1[c], c1[c], q4[c], q4s[c], s1);
+            }
           }
         }
       }
     }
+    if constexpr (kSplitDma) {
+      if (pend >= 0) issue_part(pend, std::integral_constant<int, KA>(), std::integral_constant<int, KB>());
+    }
+    s0 += t0;
+    s1 += t1;
     // the logits are consumed by VALU code: keep them out of the AGPRs that
     // hold the O accumulator
     asm volatile("" : "+v"(s0), "+v"(s1));
@@ -730,6 +782,9 @@ void stage1_kernel(Stage1Args a) {
     }
     l_run += psum;
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+    if constexpr (kSplitDma) {
+      if (pend >= 0) issue_part(pend, std::integral_constant<int, KB>(), std::integral_constant<int, Kv<KF>::kNdmaX4>());
+    }
     // ---------------- P*V
     if constexpr (KF == FBF16) {
       const int j = lane & 15;
@@ -818,10 +873,14 @@ void stage1_kernel(Stage1Args a) {
   // ---- the asynchronous pipeline
   if (nloc > 0) {
     const int nfill = min(NBUF, nloc);
+    int pend = -1;
     for (int X = 0; X < nfill; ++X) {
       if (X >= D) wait_vm<D * NDMA + D - 1>();
       issue_pid(X + D);
-      issue_tile(X);
+      // split mode: the second fill tile leaves its rest to compute(0)
+      const bool full = !kSplitDma || X == 0;
+      issue_tile(X, full);
+      if (!full) pend = X;
     }
     if constexpr (kSplitQ) {
 #pragma unroll
@@ -832,7 +891,9 @@ void stage1_kernel(Stage1Args a) {
       if constexpr (NBUF == 1) {
         wait_vm<0>();
       } else if constexpr (NBUF == 2) {
-        if (ahead >= 1) wait_vm<NDMA + 1>();
+        // issued after tile jx: the next page-id gather and the first KA
+        // DMAs of tile jx + 1 (its rest went out during the previous compute)
+        if (ahead >= 1) wait_vm<KA + 1>();
         else wait_vm<0>();
       } else {
         if (ahead >= 2) wait_vm<2 * (NDMA + 1)>();
@@ -840,12 +901,14 @@ void stage1_kernel(Stage1Args a) {
         else wait_vm<0>();
       }
       const int ubase = kSub * (w + kWaves * jx);
-      compute(jx % NBUF, min(kSub, n - ubase));
+      compute(jx % NBUF, min(kSub, n - ubase), pend);
+      pend = -1;
       const int X = jx + NBUF;
       if (X < nloc) {
         wait_vm<D * NDMA + D - 1>();
         issue_pid(X + D);
-        issue_tile(X);
+        issue_tile(X, !kSplitDma);
+        if (kSplitDma) pend = X;
       }
     }
   }

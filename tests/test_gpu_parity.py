@@ -66,6 +66,24 @@ def test_mxfp4_quantizer_bit_exact(orc):
     assert np.array_equal(u8(p_g), p_o)
 
 
+def test_quantizers_into_preallocated_outputs():
+    x = synth.normal_bf16((64, 576), seed=77, device=DEV)
+    c1, s1 = mla.quantize_fp8(x, 0.01)
+    out = torch.empty_like(c1)
+    c2, s2 = mla.quantize_fp8(x, s1, out=out)
+    assert c2.data_ptr() == out.data_ptr() and torch.equal(u8t(c1), u8t(c2))
+    p1, e1 = mla.quantize_mxfp4(x)
+    po, eo = torch.empty_like(p1), mla.mxfp4_scale_buffer(64, DEV)
+    p2, e2 = mla.quantize_mxfp4(x, out=(po, eo))
+    assert p2.data_ptr() == po.data_ptr() and torch.equal(p1, p2) and torch.equal(e1, e2)
+    with pytest.raises(ValueError):
+        mla.quantize_fp8(x, 0.01, out=torch.empty((3, 576), dtype=torch.float8_e4m3fn, device=DEV))
+
+
+def u8t(x):
+    return x.view(torch.uint8)
+
+
 # ---------------------------------------------------------------- decode
 def prepare(case, q_fmt, kv_fmt, orc, q_static=6.0 / 448.0):
     """GPU operands (GPU quantisers) and oracle operands (oracle quantisers); asserts equal codes."""
