@@ -217,6 +217,40 @@ def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
     return res, wall
 
 
+def time_ragged(steps, warmup, device, warmup_s=0.3):
+    """A ragged batch: 64 requests with seeded lognormal lengths (sigma 1, mean
+    8192 tokens; the total of bs=64 kv_len=8192), bf16 Q over the fp8 cache,
+    page 8 shuffled.  Uniform splits (the heuristic's S for the mean length)
+    against the host-planned work list."""
+    B, mean_len = 64, 8192
+    lengths = synth.ragged_lengths(B, mean_len, 1.0, synth.BASE_SEED + 50)
+    case = synth.make_case(B, lengths, 8, shuffle=True, seed=synth.BASE_SEED + 51, device=device)
+    kv, ks = mla.quantize_fp8(case["kv"])
+    q, ind, pt = case["q"], case["kv_indptr"], case["page_table"]
+    del case
+    S = mla.choose_num_splits(B, mean_len, mla.FP8)
+    items, req, ns = mla.plan_worklist(ind.cpu())
+    items_d, req_d = items.to(device), req.to(device)
+    ws = torch.empty(max(16, mla.workspace_bytes(B, S), mla.worklist_workspace_bytes(ns)), dtype=torch.uint8,
+                     device=device)
+    out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=device)
+    uni = time_calls(lambda i: mla.decode(q, kv, ind, pt, 8, S, kv_scale=ks, out=out, workspace=ws), steps, warmup,
+                     warmup_s)[0]
+    wl = time_calls(lambda i: mla.decode_worklist(q, kv, ind, pt, 8, items_d, req_d, ns, kv_scale=ks, out=out,
+                                                  workspace=ws), steps, warmup, warmup_s)[0]
+    T = sum(lengths)
+    nbytes = 576 * T + B * 16 * 1152 + 4 * math.ceil(T / 8) + 4 * (B + 1) + B * 16 * 1024
+    res = {"workload": "bs64_ragged_lognormal_a16w8", "batch": B, "kv_len_mean": mean_len,
+           "kv_len_min": min(lengths), "kv_len_max": max(lengths), "q": "bf16", "kv": "fp8", "page_size": 8,
+           "work_items": len(items), "partial_slots": ns,
+           "us_per_call": round(wl * 1e3, 3), "gbs": round(nbytes / (wl * 1e-3) / 1e9, 1),
+           "frac_of_peak": round(nbytes / (wl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "uniform_num_splits": S, "us_uniform_splits": round(uni * 1e3, 3), "compulsory_bytes": nbytes}
+    del kv, q, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_ceiling(nbytes, device, steps=50):
     """Median GB/s of the library's streaming-read probe over a buffer of
     `nbytes` bytes: the practical HBM read ceiling for a read-once kernel."""
@@ -323,6 +357,8 @@ def main():
                 continue
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             others.append(time_workload(ow, max(10, args.steps // 2), args.warmup, device, args.warmup_seconds)[0])
+        print("[bench] ragged batch (work list)", file=sys.stderr, flush=True)
+        others.append(time_ragged(max(10, args.steps // 2), args.warmup, device, args.warmup_seconds))
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -145,6 +145,59 @@ int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, i
 int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len);
 
 /*
+ * Work lists for ragged batches.  With one split count for the whole batch a
+ * long request's splits outlast everything else; a work list instead cuts
+ * every request into items of about the same token count, so one launch is
+ * balanced whatever the length mix.  Page 668813's fp8 route and page
+ * 695854's default route build the same kind of plan with aiter's metadata
+ * builder (get_mla_metadata_v1: per-CU work items, per-request reduce
+ * ranges, an fp32 partial array); this plan is built on the host.
+ *
+ * mla_plan_worklist - host planner (pure host code, no HIP call).
+ *   kv_indptr_host  host int32[batch+1] token offsets, nondecreasing.
+ *   num_cus         compute units (0 = 256).
+ *   max_items       capacity of items_host, >= batch.
+ *   items_host      out: int32[max_items][4] = {request, first token within
+ *                   the request, token count, slot}; slot indexes the item's
+ *                   partial in the workspace, or is -1 when its request is a
+ *                   single item (stage 1 then writes `out` directly).
+ *   req_host        out: int32[batch][2] = {first slot, number of items}.
+ *   num_items, num_slots  out: items written and partial slots used.
+ * The chunk is the smallest multiple of 128 tokens (at least 256, grown in
+ * steps of about 1/8 from T / (R * num_cus), T the total token count) whose
+ * items fit R = ceil(batch / num_cus) rounds of one workgroup per CU, then
+ * doubled if needed until the items fit in max_items.  A request of L tokens becomes n = ceil(L /
+ * chunk) items, item j covering tokens [floor(jL/n), floor((j+1)L/n)); an
+ * empty request one item of 0 tokens.  Items are listed request by request.
+ * Returns MLA_OK, MLA_ERR_NULL, or MLA_ERR_ARG (batch < 0, max_items < batch,
+ * decreasing offsets).
+ */
+int mla_plan_worklist(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus, int32_t max_items,
+                      int32_t* items_host, int32_t* req_host, int32_t* num_items, int32_t* num_slots);
+
+/* Bytes of workspace a plan with num_slots partial slots needs (fp32
+ * partial O [num_slots,16,512] then base-2 LSE [num_slots,16]); 0 for 0. */
+size_t mla_worklist_workspace_bytes(int32_t num_slots);
+
+/*
+ * mla_decode_worklist - mla_decode over a plan from mla_plan_worklist: one
+ * stage-1 workgroup per item, then stage 2 merges the slots of every request
+ * with more than one item.  items (int32[num_items][4]) and req
+ * (int32[batch][2]) are device copies of the planner's arrays; the other
+ * arguments are as for mla_decode, with num_splits replaced by the plan and
+ * workspace sized by mla_worklist_workspace_bytes(num_slots).  Errors as for
+ * mla_decode, plus MLA_ERR_NULL for a missing plan array and MLA_ERR_ARG for
+ * num_items < batch or num_slots < 0.  The device-resident plan is not
+ * checked, like kv_indptr.
+ */
+int mla_decode_worklist(const void* q, int32_t q_dtype, const void* q_scale,
+                        const void* kv_cache, int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows,
+                        const int32_t* kv_indptr, int32_t batch,
+                        const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                        const int32_t* items, int32_t num_items, const int32_t* req, int32_t num_slots,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_quantize_fp8 - OCP e4m3fn per-tensor quantisation of n bf16 values
  * (page 668813, the naive per-tensor fp8 quantiser): with dynamic != 0 the
  * scale is max(max|x|, 1e-12) / 448 computed on the device and written to

@@ -44,6 +44,7 @@ _DECODE_ARGS = [_c_void, _c_int32, _c_void, _c_void, _c_int32, _c_void, _c_int64
 
 EXPORTS = ("mla_decode", "mla_validate", "mla_workspace_bytes", "mla_choose_num_splits",
            "mla_recommend_page_size", "mla_quantize_fp8", "mla_quantize_mxfp4", "mla_stream_read",
+           "mla_plan_worklist", "mla_worklist_workspace_bytes", "mla_decode_worklist",
            "mla_status_string", "mla_abi_version")
 
 
@@ -77,6 +78,13 @@ def load():
             L.mla_quantize_fp8.argtypes = [_c_void, _c_int64, _c_void, _c_void, _c_int32, _c_void]
             L.mla_quantize_mxfp4.restype = ctypes.c_int
             L.mla_quantize_mxfp4.argtypes = [_c_void, _c_int64, _c_int64, _c_void, _c_void, _c_void]
+            L.mla_plan_worklist.restype = ctypes.c_int
+            L.mla_plan_worklist.argtypes = [_c_void, _c_int32, _c_int32, _c_int32, _c_void, _c_void, _c_void, _c_void]
+            L.mla_worklist_workspace_bytes.restype = _c_size
+            L.mla_worklist_workspace_bytes.argtypes = [_c_int32]
+            L.mla_decode_worklist.restype = ctypes.c_int
+            L.mla_decode_worklist.argtypes = (_DECODE_ARGS[:12] + [_c_void, _c_int32, _c_void, _c_int32]
+                                              + [_c_void, _c_void, _c_size, _c_void])
             L.mla_stream_read.restype = ctypes.c_int
             L.mla_stream_read.argtypes = [_c_void, _c_int64, _c_void, _c_void]
             L.mla_status_string.restype = ctypes.c_char_p
@@ -251,3 +259,48 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     rc = load().mla_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(stream))
     if rc:
         raise StatusError("mla_stream_read", rc)
+
+
+def plan_worklist(kv_indptr, num_cus: int = 0, max_items: int | None = None):
+    """Host work-list plan for a ragged batch (mla_plan_worklist).
+
+    kv_indptr: host int32 token offsets [B+1] (a CPU tensor, numpy array or
+    list).  Returns (items int32 [n, 4] CPU tensor {request, first token,
+    tokens, slot}, req int32 [B, 2] CPU tensor {first slot, items}, num_slots).
+    """
+    ind = torch.as_tensor(kv_indptr, dtype=torch.int32).contiguous().cpu()
+    batch = ind.numel() - 1
+    if max_items is None:
+        total = int(ind[-1] - ind[0]) if batch > 0 else 0
+        max_items = batch + total // 256 + 1
+    items = torch.empty((max(max_items, 1), 4), dtype=torch.int32)
+    req = torch.empty((max(batch, 1), 2), dtype=torch.int32)
+    n_items, n_slots = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = load().mla_plan_worklist(ind.data_ptr(), batch, int(num_cus), int(max_items), items.data_ptr(),
+                                  req.data_ptr(), ctypes.addressof(n_items), ctypes.addressof(n_slots))
+    if rc:
+        raise StatusError("mla_plan_worklist", rc)
+    return items[: n_items.value].clone(), req[:batch].clone(), n_slots.value
+
+
+def worklist_workspace_bytes(num_slots: int) -> int:
+    return int(load().mla_worklist_workspace_bytes(int(num_slots)))
+
+
+def decode_worklist(q, kv_cache, kv_indptr, page_table, page_size, items, req, num_slots, *, q_scale=None,
+                    kv_scale=None, page_indptr=None, out=None, workspace=None, stream=None):
+    """MLA decode over a work-list plan (mla_decode_worklist); items / req are
+    device copies of plan_worklist's tensors.  Returns out [batch,16,512] bf16."""
+    batch = kv_indptr.numel() - 1
+    if out is None:
+        out = torch.empty((batch, HEADS, D_V), dtype=torch.bfloat16, device=kv_cache.device)
+    if workspace is None and num_slots > 0:
+        workspace = torch.empty(worklist_workspace_bytes(num_slots), dtype=torch.uint8, device=kv_cache.device)
+    _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out, workspace, items, req)
+    args = _decode_args(q, kv_cache, kv_indptr, page_table, page_size, 1, q_scale, kv_scale, page_indptr, out,
+                        workspace)
+    rc = (_lib or load()).mla_decode_worklist(*args[:12], _ptr(items), items.shape[0], _ptr(req), int(num_slots),
+                                              *args[13:], _stream(stream))
+    if rc:
+        raise StatusError("mla_decode_worklist", rc)
+    return out

@@ -321,6 +321,8 @@ struct Stage1Args {
   float* part_o;
   float* part_lse;
   uint16_t* out;
+  const int32_t* items;  // work-list plan (int32[num_items][4]), or NULL: split grid
+  int32_t batch;
   int32_t page_size;
   int32_t num_splits;
   float sm_scale_log2e;
@@ -360,8 +362,19 @@ void stage1_kernel(Stage1Args a) {
   const int g = lane >> 4;   // MFMA lane group
   const int hq = lane & 15;  // head (QK / PV output column of the 16-wide side)
   const int S = a.num_splits;
-  const int b = blockIdx.x / S;
-  const int s = blockIdx.x - b * S;
+  // work decomposition: workgroup = (request, split) of a uniform split grid,
+  // or one item {request, first token, tokens, slot} of a work-list plan
+  int b, s = 0, slot = -1, it_t0 = 0, it_n = 0;
+  if (a.items) {
+    const int32_t* it = a.items + 4 * blockIdx.x;
+    b = min(max(it[0], 0), a.batch - 1);
+    it_t0 = it[1];
+    it_n = it[2];
+    slot = it[3];
+  } else {
+    b = blockIdx.x / S;
+    s = blockIdx.x - b * S;
+  }
 
   // ---- Q fragments (B operands) for this lane's head.  Issued first: they
   // depend on the request index only, so their latency overlaps the
@@ -425,9 +438,17 @@ void stage1_kernel(Stage1Args a) {
   if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
   const int kv0 = a.kv_indptr[b];
   const int Lr = a.kv_indptr[b + 1] - kv0;
-  const int chunk = (Lr + S - 1) / S;
-  const int t0 = s * chunk;
-  const int n = max(0, min(chunk, Lr - t0));  // tokens of this split
+  int t0, n;  // first token and token count of this workgroup's range
+  if (a.items) {
+    // clamped to the request, so a plan that disagrees with kv_indptr still
+    // only touches this request's pages
+    t0 = max(0, min(it_t0, Lr));
+    n = max(0, min(it_n, Lr - t0));
+  } else {
+    const int chunk = (Lr + S - 1) / S;
+    t0 = s * chunk;
+    n = max(0, min(chunk, Lr - t0));
+  }
   const int nsub = (n + kSub - 1) / kSub;
   const int nloc = w < nsub ? (nsub - w + kWaves - 1) / kWaves : 0;
   const uint32_t gbase = a.page_indptr ? static_cast<uint32_t>(t0) : static_cast<uint32_t>(kv0 + t0);
@@ -963,9 +984,10 @@ void stage1_kernel(Stage1Args a) {
   const float mul = nonempty ? out_mul / lsum : 0.0f;
   const float lse = nonempty ? M + __builtin_amdgcn_logf(lsum) : -__builtin_huge_valf();
   const size_t orow = static_cast<size_t>(b) * kHeads + hq;
+  const bool direct = a.items ? slot < 0 : S == 1;
   // fragment c = 8w + i; non-mxfp4 row r of fragment c is output column
   // 16c + 4g + r, mxfp4 row r is column 32(4g + r) + c
-  if (S == 1) {
+  if (direct) {
     uint16_t* op = a.out + orow * kDv;
     if constexpr (KF == FMX) {
 #pragma unroll
@@ -987,7 +1009,7 @@ void stage1_kernel(Stage1Args a) {
       }
     }
   } else {
-    const size_t prow = (static_cast<size_t>(b) * S + s) * kHeads + hq;
+    const size_t prow = (a.items ? static_cast<size_t>(slot) : static_cast<size_t>(b) * S + s) * kHeads + hq;
     float* po = a.part_o + prow * kDv;
     if constexpr (KF == FMX) {
 #pragma unroll
@@ -1012,12 +1034,20 @@ void stage1_kernel(Stage1Args a) {
 // maximum moves with a rescale of the accumulator (one load round trip for
 // S <= 8).
 __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                                     uint16_t* __restrict__ out, int S) {
+                                                     uint16_t* __restrict__ out, int S, const int32_t* __restrict__ req) {
   const int b = blockIdx.x >> 2;
   const int hq = ((blockIdx.x & 3) << 2) + (threadIdx.x >> 6);
   const int col = 8 * (threadIdx.x & 63);
-  const float* lse = part_lse + static_cast<size_t>(b) * S * kHeads + hq;
-  const float* po = part_o + (static_cast<size_t>(b) * S * kHeads + hq) * kDv + col;
+  // a request's partials: slots [base, base + S) (work list: from the plan;
+  // a single-item request was written by stage 1)
+  size_t base = static_cast<size_t>(b) * S;
+  if (req) {
+    S = req[2 * b + 1];
+    if (S <= 1) return;
+    base = static_cast<size_t>(req[2 * b]);
+  }
+  const float* lse = part_lse + base * kHeads + hq;
+  const float* po = part_o + (base * kHeads + hq) * kDv + col;
   constexpr float kNegInf = -__builtin_huge_valf();
   constexpr int kB = 8;
   float M = kNegInf, ws = 0.0f;
@@ -1175,9 +1205,16 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
 
 // ------------------------------------------------------------------ launch
 template <int QF, int KF>
-hipError_t launch_stage1(const Stage1Args& a, int batch, hipStream_t st) {
-  hipLaunchKernelGGL((stage1_kernel<QF, KF>), dim3(static_cast<unsigned>(batch) * a.num_splits), dim3(kThreads), 0, st, a);
+hipError_t launch_stage1(const Stage1Args& a, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((stage1_kernel<QF, KF>), dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_stage1_any(const Stage1Args& a, int32_t q_dtype, int32_t kv_dtype, unsigned grid, hipStream_t st) {
+  if (kv_dtype == MLA_DTYPE_BF16) return launch_stage1<FBF16, FBF16>(a, grid, st);
+  if (kv_dtype == MLA_DTYPE_FP8_E4M3FN)
+    return q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FFP8>(a, grid, st) : launch_stage1<FFP8, FFP8>(a, grid, st);
+  return q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FMX>(a, grid, st) : launch_stage1<FMX, FMX>(a, grid, st);
 }
 
 int grid_for(int64_t n, int per) {
@@ -1236,18 +1273,60 @@ int mla_decode(const void* q, int32_t q_dtype, const void* q_scale, const void* 
   a.part_o = num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = num_splits > 1 ? static_cast<float*>(workspace) + parts * kDv : nullptr;
   a.out = static_cast<uint16_t*>(out);
+  a.items = nullptr;
+  a.batch = batch;
   a.page_size = page_size;
   a.num_splits = num_splits;
   a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);  // log2(e) / sqrt(576)
-  hipError_t e;
-  if (kv_dtype == MLA_DTYPE_BF16) e = launch_stage1<FBF16, FBF16>(a, batch, st);
-  else if (kv_dtype == MLA_DTYPE_FP8_E4M3FN)
-    e = q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FFP8>(a, batch, st) : launch_stage1<FFP8, FFP8>(a, batch, st);
-  else e = q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FMX>(a, batch, st) : launch_stage1<FMX, FMX>(a, batch, st);
-  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(batch) * num_splits, st) != hipSuccess)
+    return MLA_ERR_LAUNCH;
   if (num_splits > 1) {
     hipLaunchKernelGGL(stage2_kernel, dim3(static_cast<unsigned>(batch) * 4), dim3(256), 0, st, a.part_o, a.part_lse,
-                       static_cast<uint16_t*>(out), num_splits);
+                       static_cast<uint16_t*>(out), num_splits, static_cast<const int32_t*>(nullptr));
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+int mla_decode_worklist(const void* q, int32_t q_dtype, const void* q_scale, const void* kv_cache, int32_t kv_dtype,
+                        const void* kv_scale, int64_t num_kv_rows, const int32_t* kv_indptr, int32_t batch,
+                        const int32_t* page_table, const int32_t* page_indptr, int32_t page_size, const int32_t* items,
+                        int32_t num_items, const int32_t* req, int32_t num_slots, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  // the shared argument checks (one split: no workspace demanded here)
+  int rc = mla_validate(q, q_dtype, q_scale, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch, page_table,
+                        page_indptr, page_size, 1, out, nullptr, 0);
+  if (rc != MLA_OK || batch == 0) return rc;
+  if (!items || !req) return MLA_ERR_NULL;
+  if (num_items < batch || num_slots < 0) return MLA_ERR_ARG;
+  const size_t need = mla_worklist_workspace_bytes(num_slots);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return MLA_ERR_ALIGN;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  Stage1Args a;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.kv = static_cast<const char*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.kv_indptr = kv_indptr;
+  a.page_table = page_table;
+  a.page_indptr = page_indptr;
+  const size_t parts = static_cast<size_t>(num_slots) * kHeads;
+  a.part_o = num_slots > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = num_slots > 0 ? static_cast<float*>(workspace) + parts * kDv : nullptr;
+  a.out = static_cast<uint16_t*>(out);
+  a.items = items;
+  a.batch = batch;
+  a.page_size = page_size;
+  a.num_splits = 1;
+  a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);
+  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(num_items), st) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (num_slots > 0) {
+    hipLaunchKernelGGL(stage2_kernel, dim3(static_cast<unsigned>(batch) * 4), dim3(256), 0, st, a.part_o, a.part_lse,
+                       static_cast<uint16_t*>(out), 1, req);
     if (hipGetLastError() != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;

@@ -136,6 +136,74 @@ int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, i
   return best_s;
 }
 
+int mla_plan_worklist(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus, int32_t max_items,
+                      int32_t* items_host, int32_t* req_host, int32_t* num_items, int32_t* num_slots) {
+  if (!num_items || !num_slots) return MLA_ERR_NULL;
+  *num_items = 0;
+  *num_slots = 0;
+  if (batch < 0 || max_items < batch) return MLA_ERR_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!kv_indptr_host || !items_host || !req_host) return MLA_ERR_NULL;
+  if (num_cus <= 0) num_cus = 256;
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = static_cast<int64_t>(kv_indptr_host[b + 1]) - kv_indptr_host[b];
+    if (L < 0) return MLA_ERR_ARG;
+    total += L;
+  }
+  // Aim at whole rounds of one workgroup per CU: the smallest chunk (a
+  // multiple of 128 tokens, at least 256) whose items fit ceil(batch /
+  // num_cus) rounds; each extra round would pay the per-workgroup prologue
+  // and epilogue again.
+  int64_t max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = static_cast<int64_t>(kv_indptr_host[b + 1]) - kv_indptr_host[b];
+    if (L > max_len) max_len = L;
+  }
+  const int64_t target = ((static_cast<int64_t>(batch) + num_cus - 1) / num_cus) * num_cus;
+  auto count_items = [&](int64_t c) {
+    int64_t n = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t L = static_cast<int64_t>(kv_indptr_host[b + 1]) - kv_indptr_host[b];
+      n += L > 0 ? (L + c - 1) / c : 1;
+    }
+    return n;
+  };
+  int64_t chunk = (total + target - 1) / target;
+  chunk = (chunk + 127) / 128 * 128;
+  if (chunk < 256) chunk = 256;
+  while (chunk < max_len && count_items(chunk) > target) chunk = (chunk + chunk / 8 + 127) / 128 * 128;
+  while (count_items(chunk) > max_items) chunk *= 2;
+  int32_t ni = 0, ns = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = static_cast<int64_t>(kv_indptr_host[b + 1]) - kv_indptr_host[b];
+    const int64_t n = L > 0 ? (L + chunk - 1) / chunk : 1;
+    req_host[2 * b] = n > 1 ? ns : -1;
+    req_host[2 * b + 1] = static_cast<int32_t>(n);
+    for (int64_t j = 0; j < n; ++j) {
+      // item j covers [floor(jL/n), floor((j+1)L/n)): sizes differ by at most
+      // one token and none is empty (n <= L)
+      const int64_t t0 = j * L / n;
+      const int64_t cnt = (j + 1) * L / n - t0;
+      int32_t* it = items_host + 4 * ni;
+      it[0] = b;
+      it[1] = static_cast<int32_t>(t0);
+      it[2] = static_cast<int32_t>(cnt);
+      it[3] = n > 1 ? ns++ : -1;
+      ++ni;
+    }
+  }
+  *num_items = ni;
+  *num_slots = ns;
+  return MLA_OK;
+}
+
+size_t mla_worklist_workspace_bytes(int32_t num_slots) {
+  if (num_slots <= 0) return 0;
+  const size_t parts = static_cast<size_t>(num_slots) * MLA_NUM_HEADS;
+  return parts * MLA_HEAD_DIM_V * sizeof(float) + parts * sizeof(float);
+}
+
 int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len) {
   (void)batch;
   return kv_len > 1024 ? 8 : 1;

@@ -111,6 +111,16 @@ def make_case(batch: int, lengths, page_size: int, *, shuffle: bool, seed: int, 
     }
 
 
+def ragged_lengths(batch: int, mean_len: int, sigma: float, seed: int):
+    """Seeded lognormal request lengths scaled to the given mean (each >= 1):
+    a serving-like mix of short and very long contexts for the same total
+    token count as a uniform batch."""
+    g = _gen(seed, "cpu")
+    x = torch.exp(torch.randn(batch, generator=g, dtype=torch.float64) * sigma)
+    lens = torch.clamp(torch.round(x / x.mean() * mean_len), min=1).to(torch.int64)
+    return [int(v) for v in lens]
+
+
 def workload_case(w: Workload, device="cpu", seed_offset: int = 0):
     """The synthetic instance of a named workload (seed = base + index)."""
     return make_case(w.batch, w.kv_len, w.page_size, shuffle=w.shuffle, seed=BASE_SEED + w.index + seed_offset,

@@ -262,6 +262,38 @@ def test_block_scaled_inputs(orc, qf, kf):
     check_close(out, ref, atol=2e-2 * scale, rtol=2e-2, what=f"block-scaled {qf}/{kf}")
 
 
+@pytest.mark.parametrize("qf,kf", PAIRS)
+@pytest.mark.parametrize("cus", [16, 256])
+def test_worklist_ragged_batch(orc, qf, kf, cus):
+    """Work-list decode of a ragged batch (empty, one-token, short and long
+    requests) against the oracle, and against the uniform-split path."""
+    lengths = [1, 3000, 0, 17, 9000, 256, 40, 700]
+    case = synth.make_case(len(lengths), lengths, 8, shuffle=True, seed=840)
+    g, o = prepare(case, qf, kf, orc)
+    items, req, ns = mla.plan_worklist(case["kv_indptr"].cpu(), num_cus=cus)
+    assert ns > 0 and len(items) > len(lengths)
+    out = mla.decode_worklist(g["q"], g["kv"], g["kv_indptr"], g["page_table"], case["page_size"],
+                              items.to(DEV), req.to(DEV), ns, q_scale=g["q_scale"], kv_scale=g["kv_scale"])
+    torch.cuda.synchronize()
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what=f"work list {qf}/{kf} cus={cus}")
+    assert torch.all(out[2] == 0)  # the empty request
+    uni = gpu_decode(case, g, 4)
+    check_close(out, uni.to(torch.float64).cpu().numpy(), atol=1e-2, rtol=1e-2, l2=5e-3, what="vs uniform splits")
+
+
+def test_worklist_per_request_pages(orc):
+    lengths = [513, 0, 96, 2049]
+    case = synth.make_case(len(lengths), lengths, 3, shuffle=True, seed=841, per_request_pages=True)
+    g, o = prepare(case, "bf16", "fp8", orc)
+    items, req, ns = mla.plan_worklist(case["kv_indptr"].cpu(), num_cus=4)
+    out = mla.decode_worklist(g["q"], g["kv"], g["kv_indptr"], g["page_table"], case["page_size"],
+                              items.to(DEV), req.to(DEV), ns, kv_scale=g["kv_scale"], page_indptr=g["page_indptr"])
+    torch.cuda.synchronize()
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what="work list, per-request pages")
+
+
 @pytest.mark.parametrize("S", [1, 4])
 def test_graph_replay_matches_eager(orc, S):
     """Decode captured in a HIP graph (how a serving loop issues it) gives the

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import mla_latent_kv_13_amd as mla
@@ -149,3 +150,61 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text and "liboracle" not in text, f
+
+
+def _check_plan(ind, items, req, ns, num_cus):
+    ind = [int(x) for x in ind]
+    B = len(ind) - 1
+    items, req = items.tolist(), req.tolist()
+    rounds = max(1, -(-B // num_cus))
+    assert len(items) <= rounds * num_cus  # whole rounds of one workgroup per CU
+    slots = []
+    pos = 0
+    for b in range(B):
+        L = ind[b + 1] - ind[b]
+        first, n = req[b]
+        mine = items[pos:pos + n]
+        pos += n
+        assert len(mine) == n and all(it[0] == b for it in mine)
+        if L == 0:
+            assert n == 1 and mine[0][1:3] == [0, 0]
+        # contiguous cover of [0, L), no empty item, sizes within one token
+        t = 0
+        for it in mine:
+            assert it[1] == t and it[2] >= (1 if L else 0)
+            t += it[2]
+        assert t == L
+        sizes = [it[2] for it in mine]
+        assert max(sizes) - min(sizes) <= 1
+        if n == 1:
+            assert first == -1 and mine[0][3] == -1
+        else:
+            assert [it[3] for it in mine] == list(range(first, first + n))
+            slots += [it[3] for it in mine]
+    assert pos == len(items)
+    assert sorted(slots) == list(range(ns))
+
+
+def test_worklist_planner(lib):
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        B = int(rng.integers(1, 40))
+        lens = rng.choice([0, 1, 31, 256, 1000, 5000, 70000], size=B, p=[.1, .1, .1, .2, .2, .2, .1])
+        ind = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        for cus in (8, 256):
+            items, req, ns = mla.plan_worklist(ind, num_cus=cus)
+            _check_plan(ind, items, req, ns, cus)
+
+
+def test_worklist_planner_limits(lib):
+    ind = np.array([0, 100000, 100001], dtype=np.int32)
+    items, req, ns = mla.plan_worklist(ind, num_cus=256, max_items=4)  # chunk doubles until 4 items fit
+    assert len(items) <= 4 and int(items[:, 2].sum()) == 100001
+    with pytest.raises(mla.StatusError):
+        mla.plan_worklist(ind, max_items=1)  # fewer items than requests
+    with pytest.raises(mla.StatusError):
+        mla.plan_worklist(np.array([0, 5, 3], dtype=np.int32))  # decreasing offsets
+    items, req, ns = mla.plan_worklist(np.array([0], dtype=np.int32))
+    assert len(items) == 0 and ns == 0
+    assert lib.mla_worklist_workspace_bytes(0) == 0
+    assert lib.mla_worklist_workspace_bytes(3) == 3 * 16 * 513 * 4
