@@ -41,9 +41,9 @@ _DTYPES = {"bf16": BF16, "fp8": FP8, "mxfp4": MXFP4}
 def build(force: bool = True) -> str:
     """Compile oracle.c into _build/liboracle.so with gcc (OpenMP, no fast-math)."""
     os.makedirs(_BUILD, exist_ok=True)
-    if not force and os.path.exists(_LIB_PATH):
-        return _LIB_PATH
     src = os.path.join(_HERE, "oracle.c")
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(src):
+        return _LIB_PATH
     tmp = _LIB_PATH + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
            "-ffp-contract=off", src, "-o", tmp, "-lm"]
@@ -69,6 +69,7 @@ class _Problem(ctypes.Structure):
         ("page_table", ctypes.c_void_p),
         ("page_table_len", ctypes.c_int64),
         ("page_size", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
     ]
 
 
@@ -76,8 +77,7 @@ def lib():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH):
-                build(force=False)
+            build(force=False)  # compiles only when missing or older than oracle.c
             L = ctypes.CDLL(_LIB_PATH)
             L.orc_bf16_to_f64.restype = ctypes.c_double
             L.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
@@ -199,9 +199,11 @@ def decode(q, kv, kv_indptr, page_table, page_size, *, q_dtype="bf16", kv_dtype=
            num_splits=0, pairs=None, nthreads=None):
     """fp64 MLA decode.
 
-    q        : bf16 bits [B,16,576] | e4m3fn codes [B,16,576] | packed mxfp4 [B,16,288]
+    q        : bf16 bits [B,rows,576] | e4m3fn codes [B,rows,576] | packed mxfp4 [B,rows,288]
+               (rows = q_seq_len x heads query rows per request; 16 for
+               single-token decode with 16 heads)
     kv       : physical rows, bf16 bits [R,576] | e4m3fn [R,576] | packed [R,288]
-    returns  : (out_f64 [B,16,512], out_bf16_bits [B,16,512]); rows of pairs not
+    returns  : (out_f64 [B,rows,512], out_bf16_bits [B,rows,512]); rows of pairs not
                selected (when ``pairs`` is given) are NaN / 0.
     """
     qd, kd = _DTYPES[q_dtype], _DTYPES[kv_dtype]
@@ -229,8 +231,10 @@ def decode(q, kv, kv_indptr, page_table, page_size, *, q_dtype="bf16", kv_dtype=
     P.page_table = _ptr(pt)
     P.page_table_len = pt.size
     P.page_size = int(page_size)
-    out = np.full((B, HEADS, D_V), np.nan, dtype=np.float64)
-    outb = np.zeros((B, HEADS, D_V), dtype=np.uint16)
+    rows = (qa.size // (B * (288 if qd == MXFP4 else 576))) if B > 0 else HEADS
+    P.rows = rows
+    out = np.full((B, rows, D_V), np.nan, dtype=np.float64)
+    outb = np.zeros((B, rows, D_V), dtype=np.uint16)
     sel = None
     if pairs is not None:
         sel = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))

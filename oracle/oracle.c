@@ -238,9 +238,9 @@ int orc_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* pack
 typedef struct {
   int32_t batch;
   int32_t q_dtype;
-  const void* q;         /* bf16 [B,16,576] | e4m3fn [B,16,576] | packed [B,16,288] */
+  const void* q;         /* bf16 [B,rows,576] | e4m3fn [B,rows,576] | packed [B,rows,288] */
   double q_scale;        /* fp8 Q per-tensor scale */
-  const uint8_t* q_e8m0; /* mxfp4 Q scales [B*16, 18] */
+  const uint8_t* q_e8m0; /* mxfp4 Q scales [B*rows, 18] */
   int32_t kv_dtype;
   const void* kv;        /* physical rows: bf16 [R,576] | e4m3fn [R,576] | packed [R,288] */
   int64_t kv_rows;
@@ -251,6 +251,7 @@ typedef struct {
   const int32_t* page_table;
   int64_t page_table_len;
   int32_t page_size;
+  int32_t rows; /* query rows per request (q_seq_len x heads); 0 means 16 */
 } orc_problem;
 
 static void deq_row(int dtype, const void* base, int64_t row, double scale, const uint8_t* e8m0, double* out) {
@@ -299,8 +300,12 @@ static int check_problem(const orc_problem* P) {
 
 /*
  * Unsplit decode of the (b, h) pairs listed in sel (2*nsel ints), or of every
- * pair when sel is NULL.  Writes o in fp64 and its bf16 rounding, both laid out
- * [B, 16, 512]; pairs not selected are left untouched.  num_splits == 0 means
+ * pair when sel is NULL; h is a query row of request b (rows per request:
+ * P->rows, 16 by default).  Every query row of a request attends to the
+ * request's whole cache with no mask: page 695854's chunked torch fallback
+ * (_run_chunked_torch_attention) treats q_seq_len x num_heads rows this way.
+ * Writes o in fp64 and its bf16 rounding, both laid out [B, rows, 512]; pairs
+ * not selected are left untouched.  num_splits == 0 means
  * one softmax over the whole request; num_splits >= 1 runs the split-wise
  * partial/merge form.  nthreads > 0 sets the OpenMP thread count.
  */
@@ -309,20 +314,21 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
   int rc = check_problem(P);
   if (rc) return rc;
   if (num_splits < 0) return ORC_EARG;
-  int64_t npairs = sel ? nsel : (int64_t)P->batch * ORC_HEADS;
+  const int rows = P->rows > 0 ? P->rows : ORC_HEADS;
+  int64_t npairs = sel ? nsel : (int64_t)P->batch * rows;
   int bad = 0;
   if (nthreads <= 0) nthreads = 1;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
   for (int64_t pi = 0; pi < npairs; pi++) {
-    int b = sel ? sel[2 * pi] : (int)(pi / ORC_HEADS);
-    int h = sel ? sel[2 * pi + 1] : (int)(pi % ORC_HEADS);
-    if (b < 0 || b >= P->batch || h < 0 || h >= ORC_HEADS) {
+    int b = sel ? sel[2 * pi] : (int)(pi / rows);
+    int h = sel ? sel[2 * pi + 1] : (int)(pi % rows);
+    if (b < 0 || b >= P->batch || h < 0 || h >= rows) {
       bad |= 1;
       continue;
     }
     int64_t L = (int64_t)P->kv_indptr[b + 1] - P->kv_indptr[b];
     double q[ORC_DQK], k[ORC_DQK];
-    int64_t qrow = (int64_t)b * ORC_HEADS + (g_mutation == 5 ? (h ^ 1) : h);
+    int64_t qrow = (int64_t)b * rows + (g_mutation == 5 ? (h ^ 1) : h);
     deq_row(P->q_dtype, P->q, qrow, P->q_scale, P->q_e8m0, q);
     double* o = (double*)calloc(ORC_DV, sizeof(double));
     double* s = (double*)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
@@ -386,7 +392,7 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
     }
     if (!(bad & 2)) {
       for (int i = 0; i < ORC_DV; i++) {
-        size_t idx = ((size_t)b * ORC_HEADS + h) * ORC_DV + i;
+        size_t idx = ((size_t)b * rows + h) * ORC_DV + i;
         if (out_f64) out_f64[idx] = o[i];
         if (out_bf16) out_bf16[idx] = orc_f64_to_bf16(o[i]);
       }

@@ -186,11 +186,31 @@ def pin_mxfp4_sdpa(orc):
     return pin_sdpa(orc, "mxfp4", seed=20)
 
 
+def pin_sdpa_multi_row(orc, fmt="fp8", rows=64):
+    """rows query rows per request (q_seq_len 4 x 16 heads), each attending to
+    the request's whole cache: torch SDPA with the rows as heads."""
+    case = synth.make_case(3, [17, 5, 9], 4, shuffle=True, seed=25, extra_pages=2)
+    q = synth.normal_bf16((3, rows, 576), seed=26)
+    kvd, extra, deq = rows_f64(case, fmt, orc)
+    out, _ = orc.decode(bits(q), kvd, case["kv_indptr"].numpy(), case["page_table"].numpy(), case["page_size"],
+                        kv_dtype=fmt, **extra)
+    ref = np.zeros((3, rows, 512))
+    for b in range(3):
+        L = case["lengths"][b]
+        k = torch.from_numpy(deq[logical_rows(case, b, L)])
+        qq = q[b].to(torch.float64).reshape(1, rows, 1, 576)
+        kk = k.reshape(1, 1, L, 576).expand(1, rows, L, 576)
+        vv = k[:, :512].reshape(1, 1, L, 512).expand(1, rows, L, 512)
+        ref[b] = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv).reshape(rows, 512).numpy()
+    return out.shape == (3, rows, 512) and np.allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
 PINS = {
     "sdpa_bf16": lambda o: pin_sdpa(o, "bf16"),
     "sdpa_bf16_per_request_pages": lambda o: pin_sdpa(o, "bf16", per_request=True),
     "sdpa_fp8": lambda o: pin_sdpa(o, "fp8"),
     "sdpa_mxfp4": pin_mxfp4_sdpa,
+    "sdpa_multi_row": pin_sdpa_multi_row,
     "one_token": pin_one_token,
     "two_tokens": pin_two_tokens,
     "constant_logits": pin_constant_logits,
@@ -243,6 +263,18 @@ def test_planted_mistake_fails_a_pin(orc, mutation):
     finally:
         orc.set_mutation(0)
     assert failed, f"mutation {mutation} passed every pin"
+
+
+def test_multi_row_equals_row_slices(orc):
+    """A request's 64 query rows decode exactly as four 16-row problems."""
+    case = synth.make_case(2, [40, 13], 8, shuffle=True, seed=27)
+    q = synth.normal_bf16((2, 64, 576), seed=28)
+    args = (bits(case["kv"]), case["kv_indptr"].numpy(), case["page_table"].numpy(), case["page_size"])
+    full, fullb = orc.decode(bits(q), *args)
+    for g in range(4):
+        part, partb = orc.decode(bits(q[:, 16 * g:16 * g + 16].contiguous()), *args)
+        assert np.array_equal(full[:, 16 * g:16 * g + 16], part)
+        assert np.array_equal(fullb[:, 16 * g:16 * g + 16], partb)
 
 
 def test_index_errors_are_reported(orc):
