@@ -251,6 +251,34 @@ def time_ragged(steps, warmup, device, warmup_s=0.3):
     return res
 
 
+def time_multi_token(steps, warmup, device, warmup_s=0.3):
+    """Multi-token decode: bs=64, kv_len=8192, 4 query tokens x 16 heads = 64
+    query rows per request over the fp8 cache (page 8, shuffled), bf16 Q.
+    Compulsory bytes count the cache once; split count from the heuristic
+    with the 4 query groups per request counted as workgroups."""
+    B, L, rows = 64, 8192, 64
+    case = synth.make_case(B, L, 8, shuffle=True, seed=synth.BASE_SEED + 60, device=device)
+    kv, ks = mla.quantize_fp8(case["kv"])
+    q = synth.normal_bf16((B, rows, 576), seed=synth.BASE_SEED + 61, device=device)
+    ind, pt = case["kv_indptr"], case["page_table"]
+    del case
+    S = mla.choose_num_splits(B * rows // 16, L, mla.FP8)
+    ws = torch.empty(max(16, mla.workspace_bytes(B, S, rows)), dtype=torch.uint8, device=device)
+    out = torch.empty((B, rows, 512), dtype=torch.bfloat16, device=device)
+    ms = time_calls(lambda i: mla.decode(q, kv, ind, pt, 8, S, kv_scale=ks, out=out, workspace=ws), steps, warmup,
+                    warmup_s)[0]
+    T = B * L
+    nbytes = 576 * T + B * rows * 1152 + 4 * (T // 8) + 4 * (B + 1) + B * rows * 1024
+    res = {"workload": "bs64_kv8192_q4x16_a16w8", "batch": B, "kv_len": L, "q_rows": rows, "q": "bf16", "kv": "fp8",
+           "page_size": 8, "num_splits": S, "us_per_call": round(ms * 1e3, 3),
+           "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "tflops": round(2 * rows * T * (576 + 512) / (ms * 1e-3) / 1e12, 2), "compulsory_bytes": nbytes}
+    del kv, q, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_ceiling(nbytes, device, steps=50):
     """Median GB/s of the library's streaming-read probe over a buffer of
     `nbytes` bytes: the practical HBM read ceiling for a read-once kernel."""
@@ -359,6 +387,8 @@ def main():
             others.append(time_workload(ow, max(10, args.steps // 2), args.warmup, device, args.warmup_seconds)[0])
         print("[bench] ragged batch (work list)", file=sys.stderr, flush=True)
         others.append(time_ragged(max(10, args.steps // 2), args.warmup, device, args.warmup_seconds))
+        print("[bench] multi-token decode (64 query rows)", file=sys.stderr, flush=True)
+        others.append(time_multi_token(max(10, args.steps // 2), args.warmup, device, args.warmup_seconds))
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -64,6 +64,7 @@ extern "C" {
 #define MLA_ERR_DEVICE (-7)      /* no usable gfx950 device */
 
 #define MLA_MAX_SPLITS 256
+#define MLA_MAX_Q_ROWS 1024      /* query rows per request (q_seq_len x heads), multiple of 16 */
 
 /*
  * mla_decode - split-K MLA decode of `batch` single-token requests.
@@ -145,6 +146,30 @@ int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, i
 int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len);
 
 /*
+ * mla_decode_rows - mla_decode for q_rows query rows per request: q_seq_len
+ * query tokens x num_heads heads (multi-token decode, or more than 16 heads),
+ * flattened row-major into q [batch, q_rows, 576] (mxfp4: [batch, q_rows,
+ * 288] with e8m0 q_scale [batch*q_rows, 18]); out is [batch, q_rows, 512].
+ * Every row attends to its request's whole cache with no mask, as page
+ * 695854's chunked torch fallback treats q_seq_len x num_heads rows (its
+ * aiter route takes q_seq_len 4 with 16, 32 or 64 heads).  q_rows is a
+ * multiple of 16 in 16..MLA_MAX_Q_ROWS; the kernels run one workgroup per
+ * 16-row group, the groups sharing a token range back to back so the cache
+ * is re-read from the cache hierarchy rather than HBM.  Workspace:
+ * mla_workspace_bytes_rows(batch, q_rows, num_splits).  q_rows == 16 is
+ * mla_decode.  Errors as mla_decode, plus MLA_ERR_ARG for a bad q_rows.
+ */
+int mla_decode_rows(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows,
+                    const void* kv_cache, int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows,
+                    const int32_t* kv_indptr, int32_t batch,
+                    const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                    int32_t num_splits, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of mla_decode_rows (0 when num_splits == 1 or arguments
+ * are out of range); mla_workspace_bytes(b, s) == mla_workspace_bytes_rows(b, 16, s). */
+size_t mla_workspace_bytes_rows(int32_t batch, int32_t q_rows, int32_t num_splits);
+
+/*
  * Work lists for ragged batches.  With one split count for the whole batch a
  * long request's splits outlast everything else; a work list instead cuts
  * every request into items of about the same token count, so one launch is
@@ -175,22 +200,23 @@ int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len);
 int mla_plan_worklist(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus, int32_t max_items,
                       int32_t* items_host, int32_t* req_host, int32_t* num_items, int32_t* num_slots);
 
-/* Bytes of workspace a plan with num_slots partial slots needs (fp32
- * partial O [num_slots,16,512] then base-2 LSE [num_slots,16]); 0 for 0. */
-size_t mla_worklist_workspace_bytes(int32_t num_slots);
+/* Bytes of workspace a plan with num_slots partial slots needs for q_rows
+ * query rows per request (fp32 partial O [num_slots,q_rows,512] then base-2
+ * LSE [num_slots,q_rows]); 0 for 0 slots or a bad q_rows. */
+size_t mla_worklist_workspace_bytes(int32_t num_slots, int32_t q_rows);
 
 /*
  * mla_decode_worklist - mla_decode over a plan from mla_plan_worklist: one
  * stage-1 workgroup per item, then stage 2 merges the slots of every request
  * with more than one item.  items (int32[num_items][4]) and req
  * (int32[batch][2]) are device copies of the planner's arrays; the other
- * arguments are as for mla_decode, with num_splits replaced by the plan and
- * workspace sized by mla_worklist_workspace_bytes(num_slots).  Errors as for
+ * arguments are as for mla_decode_rows, with num_splits replaced by the plan
+ * and workspace sized by mla_worklist_workspace_bytes(num_slots, q_rows).  Errors as for
  * mla_decode, plus MLA_ERR_NULL for a missing plan array and MLA_ERR_ARG for
  * num_items < batch or num_slots < 0.  The device-resident plan is not
  * checked, like kv_indptr.
  */
-int mla_decode_worklist(const void* q, int32_t q_dtype, const void* q_scale,
+int mla_decode_worklist(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows,
                         const void* kv_cache, int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows,
                         const int32_t* kv_indptr, int32_t batch,
                         const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,

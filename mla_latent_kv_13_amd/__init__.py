@@ -44,7 +44,8 @@ _DECODE_ARGS = [_c_void, _c_int32, _c_void, _c_void, _c_int32, _c_void, _c_int64
 
 EXPORTS = ("mla_decode", "mla_validate", "mla_workspace_bytes", "mla_choose_num_splits",
            "mla_recommend_page_size", "mla_quantize_fp8", "mla_quantize_mxfp4", "mla_stream_read",
-           "mla_plan_worklist", "mla_worklist_workspace_bytes", "mla_decode_worklist",
+           "mla_plan_worklist", "mla_worklist_workspace_bytes", "mla_decode_worklist", "mla_decode_rows",
+           "mla_workspace_bytes_rows",
            "mla_status_string", "mla_abi_version")
 
 
@@ -81,10 +82,15 @@ def load():
             L.mla_plan_worklist.restype = ctypes.c_int
             L.mla_plan_worklist.argtypes = [_c_void, _c_int32, _c_int32, _c_int32, _c_void, _c_void, _c_void, _c_void]
             L.mla_worklist_workspace_bytes.restype = _c_size
-            L.mla_worklist_workspace_bytes.argtypes = [_c_int32]
+            L.mla_worklist_workspace_bytes.argtypes = [_c_int32, _c_int32]
+            _rows_args = _DECODE_ARGS[:3] + [_c_int32] + _DECODE_ARGS[3:12]
             L.mla_decode_worklist.restype = ctypes.c_int
-            L.mla_decode_worklist.argtypes = (_DECODE_ARGS[:12] + [_c_void, _c_int32, _c_void, _c_int32]
+            L.mla_decode_worklist.argtypes = (_rows_args + [_c_void, _c_int32, _c_void, _c_int32]
                                               + [_c_void, _c_void, _c_size, _c_void])
+            L.mla_decode_rows.restype = ctypes.c_int
+            L.mla_decode_rows.argtypes = _rows_args + [_c_int32, _c_void, _c_void, _c_size, _c_void]
+            L.mla_workspace_bytes_rows.restype = _c_size
+            L.mla_workspace_bytes_rows.argtypes = [_c_int32, _c_int32, _c_int32]
             L.mla_stream_read.restype = ctypes.c_int
             L.mla_stream_read.argtypes = [_c_void, _c_int64, _c_void, _c_void]
             L.mla_status_string.restype = ctypes.c_char_p
@@ -128,8 +134,8 @@ def _dev(*ts):
                 raise ValueError("all tensors must be contiguous")
 
 
-def workspace_bytes(batch: int, num_splits: int) -> int:
-    return int(load().mla_workspace_bytes(int(batch), int(num_splits)))
+def workspace_bytes(batch: int, num_splits: int, q_rows: int = HEADS) -> int:
+    return int(load().mla_workspace_bytes_rows(int(batch), int(q_rows), int(num_splits)))
 
 
 def choose_num_splits(batch: int, kv_len: int, kv_dtype: int, num_cus: int = 0) -> int:
@@ -160,28 +166,48 @@ def validate(q, kv_cache, kv_indptr, page_table, page_size, num_splits, *, q_sca
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Tensor,
            page_size: int, num_splits: int | None = None, *, q_scale=None, kv_scale=None,
            page_indptr=None, out=None, workspace=None, kv_len_hint: int | None = None, stream=None):
-    """MLA decode; returns out [batch,16,512] bf16 (enqueued on the current stream).
+    """MLA decode; returns out [batch,R,512] bf16 (enqueued on the current stream).
 
-    q          [B,16,576] bf16 / float8_e4m3fn, or [B,16,288] uint8 (mxfp4, with q_scale e8m0 [B*16,18])
+    q          [B,R,576] bf16 / float8_e4m3fn, or [B,R,288] uint8 (mxfp4, with q_scale e8m0 [B*R,18]);
+               R = q_seq_len x heads query rows per request (16 for single-token decode)
     kv_cache   [R,576] bf16 / float8_e4m3fn, or [R,288] uint8 (mxfp4, with kv_scale e8m0 [R,18])
     kv_indptr  int32 [B+1] token offsets; page_table int32 page ids; page_indptr optional int32 [B]
     """
     batch = kv_indptr.numel() - 1
+    rows = _q_rows(q, batch)
     if num_splits is None:
+        # one workgroup per 16-row query group: the occupancy is batch x groups
         hint = kv_len_hint if kv_len_hint is not None else max(1, kv_cache.shape[0] // max(batch, 1))
-        num_splits = choose_num_splits(batch, hint, _fmt(kv_cache))
+        num_splits = choose_num_splits(batch * (rows // HEADS), hint, _fmt(kv_cache))
     if out is None:
-        out = torch.empty((batch, HEADS, D_V), dtype=torch.bfloat16, device=kv_cache.device)
+        out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=kv_cache.device)
     if workspace is None and batch > 0:
-        need = workspace_bytes(batch, num_splits)
+        need = workspace_bytes(batch, num_splits, rows)
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=kv_cache.device)
     _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out, workspace)
-    rc = (_lib or load()).mla_decode(*_decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale,
-                                         kv_scale, page_indptr, out, workspace), _stream(stream))
+    args = _decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale, kv_scale, page_indptr,
+                        out, workspace)
+    L = _lib or load()
+    if rows == HEADS:
+        rc = L.mla_decode(*args, _stream(stream))
+    else:
+        rc = L.mla_decode_rows(*args[:3], rows, *args[3:], _stream(stream))
     if rc:
-        raise StatusError("mla_decode", rc)
+        raise StatusError("mla_decode" if rows == HEADS else "mla_decode_rows", rc)
     return out
+
+
+def _q_rows(q, batch: int) -> int:
+    """Query rows per request from Q's element count (576 values, or 288 packed
+    bytes, per row)."""
+    if batch <= 0:
+        return HEADS
+    per_row = 288 if q.dtype == torch.uint8 else 576
+    n = q.numel() // per_row
+    if n % batch:
+        raise ValueError("q does not hold a whole number of rows per request")
+    return n // batch
 
 
 def quantize_fp8(x: torch.Tensor, scale: torch.Tensor | float | None = None, stream=None, out=None):
@@ -283,8 +309,8 @@ def plan_worklist(kv_indptr, num_cus: int = 0, max_items: int | None = None):
     return items[: n_items.value].clone(), req[:batch].clone(), n_slots.value
 
 
-def worklist_workspace_bytes(num_slots: int) -> int:
-    return int(load().mla_worklist_workspace_bytes(int(num_slots)))
+def worklist_workspace_bytes(num_slots: int, q_rows: int = HEADS) -> int:
+    return int(load().mla_worklist_workspace_bytes(int(num_slots), int(q_rows)))
 
 
 def decode_worklist(q, kv_cache, kv_indptr, page_table, page_size, items, req, num_slots, *, q_scale=None,
@@ -292,15 +318,16 @@ def decode_worklist(q, kv_cache, kv_indptr, page_table, page_size, items, req, n
     """MLA decode over a work-list plan (mla_decode_worklist); items / req are
     device copies of plan_worklist's tensors.  Returns out [batch,16,512] bf16."""
     batch = kv_indptr.numel() - 1
+    rows = _q_rows(q, batch)
     if out is None:
-        out = torch.empty((batch, HEADS, D_V), dtype=torch.bfloat16, device=kv_cache.device)
+        out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=kv_cache.device)
     if workspace is None and num_slots > 0:
-        workspace = torch.empty(worklist_workspace_bytes(num_slots), dtype=torch.uint8, device=kv_cache.device)
+        workspace = torch.empty(worklist_workspace_bytes(num_slots, rows), dtype=torch.uint8, device=kv_cache.device)
     _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out, workspace, items, req)
     args = _decode_args(q, kv_cache, kv_indptr, page_table, page_size, 1, q_scale, kv_scale, page_indptr, out,
                         workspace)
-    rc = (_lib or load()).mla_decode_worklist(*args[:12], _ptr(items), items.shape[0], _ptr(req), int(num_slots),
-                                              *args[13:], _stream(stream))
+    rc = (_lib or load()).mla_decode_worklist(*args[:3], rows, *args[3:12], _ptr(items), items.shape[0], _ptr(req),
+                                              int(num_slots), *args[13:], _stream(stream))
     if rc:
         raise StatusError("mla_decode_worklist", rc)
     return out

@@ -323,6 +323,7 @@ struct Stage1Args {
   uint16_t* out;
   const int32_t* items;  // work-list plan (int32[num_items][4]), or NULL: split grid
   int32_t batch;
+  int32_t groups;        // 16-row query groups per request (q_seq_len x heads / 16)
   int32_t page_size;
   int32_t num_splits;
   float sm_scale_log2e;
@@ -363,18 +364,25 @@ void stage1_kernel(Stage1Args a) {
   const int hq = lane & 15;  // head (QK / PV output column of the 16-wide side)
   const int S = a.num_splits;
   // work decomposition: workgroup = (request, split) of a uniform split grid,
-  // or one item {request, first token, tokens, slot} of a work-list plan
+  // or one item {request, first token, tokens, slot} of a work-list plan,
+  // times the request's G 16-row query groups (the fastest index, so the
+  // workgroups sharing a token range are dispatched together and re-read it
+  // from cache)
+  const int G = a.groups;
   int b, s = 0, slot = -1, it_t0 = 0, it_n = 0;
+  const int unit = blockIdx.x / G;
+  const int r = blockIdx.x - unit * G;
   if (a.items) {
-    const int32_t* it = a.items + 4 * blockIdx.x;
+    const int32_t* it = a.items + 4 * unit;
     b = min(max(it[0], 0), a.batch - 1);
     it_t0 = it[1];
     it_n = it[2];
     slot = it[3];
   } else {
-    b = blockIdx.x / S;
-    s = blockIdx.x - b * S;
+    b = unit / S;
+    s = unit - b * S;
   }
+  const int v = b * G + r;  // query group: Q and output rows 16v .. 16v + 15
 
   // ---- Q fragments (B operands) for this lane's head.  Issued first: they
   // depend on the request index only, so their latency overlaps the
@@ -396,7 +404,7 @@ void stage1_kernel(Stage1Args a) {
   uint32_t q4s[QF == FMX ? NQ : 1];
   float qs = 1.0f, ks = 1.0f;
   if constexpr (kSplitQ) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
 #pragma unroll
     for (int c = 0; c < NQ; ++c)
 #pragma unroll
@@ -409,18 +417,18 @@ void stage1_kernel(Stage1Args a) {
         if (d < kDqk) qraw[4 * c + j] = *reinterpret_cast<const u32x4_t*>(qrow + d);
       }
   } else if constexpr (QF == FBF16) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
 #pragma unroll
     for (int m = 0; m < NQ; ++m) qb[m] = *reinterpret_cast<const bf16x8_t*>(qrow + qdim_bf16<KF>(m, g));
   } else if constexpr (QF == FFP8) {
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + (static_cast<size_t>(b) * kHeads + hq) * kDqk;
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
 #pragma unroll
     for (int c = 0; c < 4; ++c) q8[c] = *reinterpret_cast<const i32x8_t*>(qrow + 128 * c + 32 * g);
     q8[4] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
     if (g < 2) q8[4] = *reinterpret_cast<const i32x8_t*>(qrow + 512 + 32 * g);
     qs = *static_cast<const float*>(a.q_scale);
   } else {
-    const size_t qr = static_cast<size_t>(b) * kHeads + hq;
+    const size_t qr = static_cast<size_t>(v) * kHeads + hq;
     const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * MLA_MXFP4_ROW_BYTES;
     const uint8_t* qsc = static_cast<const uint8_t*>(a.q_scale) + qr * MLA_MXFP4_ROW_SCALES;
 #pragma unroll
@@ -983,7 +991,7 @@ void stage1_kernel(Stage1Args a) {
   const bool nonempty = lsum > 0.0f;
   const float mul = nonempty ? out_mul / lsum : 0.0f;
   const float lse = nonempty ? M + __builtin_amdgcn_logf(lsum) : -__builtin_huge_valf();
-  const size_t orow = static_cast<size_t>(b) * kHeads + hq;
+  const size_t orow = static_cast<size_t>(v) * kHeads + hq;
   const bool direct = a.items ? slot < 0 : S == 1;
   // fragment c = 8w + i; non-mxfp4 row r of fragment c is output column
   // 16c + 4g + r, mxfp4 row r is column 32(4g + r) + c
@@ -1009,7 +1017,8 @@ void stage1_kernel(Stage1Args a) {
       }
     }
   } else {
-    const size_t prow = (a.items ? static_cast<size_t>(slot) : static_cast<size_t>(b) * S + s) * kHeads + hq;
+    const size_t prow =
+        ((a.items ? static_cast<size_t>(slot) : static_cast<size_t>(b) * S + s) * G + r) * kHeads + hq;
     float* po = a.part_o + prow * kDv;
     if constexpr (KF == FMX) {
 #pragma unroll
@@ -1034,20 +1043,25 @@ void stage1_kernel(Stage1Args a) {
 // maximum moves with a rescale of the accumulator (one load round trip for
 // S <= 8).
 __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                                     uint16_t* __restrict__ out, int S, const int32_t* __restrict__ req) {
-  const int b = blockIdx.x >> 2;
+                                                     uint16_t* __restrict__ out, int S, const int32_t* __restrict__ req,
+                                                     int G) {
+  const int v = blockIdx.x >> 2;  // query group (request b, group r)
+  const int b = v / G;
+  const int r = v - b * G;
   const int hq = ((blockIdx.x & 3) << 2) + (threadIdx.x >> 6);
   const int col = 8 * (threadIdx.x & 63);
   // a request's partials: slots [base, base + S) (work list: from the plan;
-  // a single-item request was written by stage 1)
+  // a single-item request was written by stage 1); slot si of group r holds
+  // rows ((base + si) * G + r) * 16 + [0, 16)
   size_t base = static_cast<size_t>(b) * S;
   if (req) {
     S = req[2 * b + 1];
     if (S <= 1) return;
     base = static_cast<size_t>(req[2 * b]);
   }
-  const float* lse = part_lse + base * kHeads + hq;
-  const float* po = part_o + (base * kHeads + hq) * kDv + col;
+  const size_t stride = static_cast<size_t>(G) * kHeads;  // rows between consecutive splits
+  const float* lse = part_lse + (base * G + r) * kHeads + hq;
+  const float* po = part_o + ((base * G + r) * kHeads + hq) * kDv + col;
   constexpr float kNegInf = -__builtin_huge_valf();
   constexpr int kB = 8;
   float M = kNegInf, ws = 0.0f;
@@ -1058,9 +1072,9 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
       const int si = min(s0 + i, S - 1);  // past the end: a repeat, weighted 0 below
-      l[i] = lse[si * kHeads];
-      x0[i] = *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(si) * kHeads * kDv);
-      x1[i] = *reinterpret_cast<const f32x4_t*>(po + static_cast<size_t>(si) * kHeads * kDv + 4);
+      l[i] = lse[si * stride];
+      x0[i] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv);
+      x1[i] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv + 4);
     }
 #pragma unroll
     for (int i = 0; i < kB; ++i)
@@ -1091,7 +1105,7 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
   o.y = bits(bf16x2_t{static_cast<__bf16>(a0.z), static_cast<__bf16>(a0.w)});
   o.z = bits(bf16x2_t{static_cast<__bf16>(a1.x), static_cast<__bf16>(a1.y)});
   o.w = bits(bf16x2_t{static_cast<__bf16>(a1.z), static_cast<__bf16>(a1.w)});
-  *reinterpret_cast<u32x4_t*>(out + (static_cast<size_t>(b) * kHeads + hq) * kDv + col) = o;
+  *reinterpret_cast<u32x4_t*>(out + (static_cast<size_t>(v) * kHeads + hq) * kDv + col) = o;
 }
 
 // -------------------------------------------------------------- quantisers
@@ -1248,6 +1262,60 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Shared launcher: uniform splits (items == NULL) or a work-list plan, for
+// q_rows query rows per request (G = q_rows / 16 query groups).
+int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows, const void* kv_cache,
+                  int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows, const int32_t* kv_indptr,
+                  int32_t batch, const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                  int32_t num_splits, const int32_t* items, int32_t num_items, const int32_t* req, int32_t num_slots,
+                  void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q_rows < kHeads || q_rows % kHeads || q_rows > MLA_MAX_Q_ROWS) return MLA_ERR_ARG;
+  const int G = q_rows / kHeads;
+  // the shared argument checks, without the workspace (sized per mode below)
+  int rc = mla_validate(q, q_dtype, q_scale, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch, page_table,
+                        page_indptr, page_size, items ? 1 : num_splits, out, nullptr, 0);
+  if (rc == MLA_ERR_WORKSPACE) rc = MLA_OK;  // checked below
+  if (rc != MLA_OK || batch == 0) return rc;
+  if (items && (!req)) return MLA_ERR_NULL;
+  if (items && (num_items < batch || num_slots < 0)) return MLA_ERR_ARG;
+  const int64_t units = items ? static_cast<int64_t>(num_items) : static_cast<int64_t>(batch) * num_splits;
+  if (units * G > 0x7fffffffLL || static_cast<int64_t>(batch) * G * 4 > 0x7fffffffLL) return MLA_ERR_ARG;
+  const int64_t nslots = items ? num_slots : (num_splits > 1 ? static_cast<int64_t>(batch) * num_splits : 0);
+  const size_t parts = static_cast<size_t>(nslots) * G * kHeads;
+  const size_t need = parts * kDv * sizeof(float) + parts * sizeof(float);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return MLA_ERR_ALIGN;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so it is not misattributed
+  Stage1Args a;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.kv = static_cast<const char*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.kv_indptr = kv_indptr;
+  a.page_table = page_table;
+  a.page_indptr = page_indptr;
+  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = need ? static_cast<float*>(workspace) + parts * kDv : nullptr;
+  a.out = static_cast<uint16_t*>(out);
+  a.items = items;
+  a.batch = batch;
+  a.groups = G;
+  a.page_size = page_size;
+  a.num_splits = items ? 1 : num_splits;
+  a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);  // log2(e) / sqrt(576)
+  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(units * G), st) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  if (need) {
+    hipLaunchKernelGGL(stage2_kernel, dim3(static_cast<unsigned>(batch) * G * 4), dim3(256), 0, st, a.part_o,
+                       a.part_lse, static_cast<uint16_t*>(out), items ? 1 : num_splits, items ? req : nullptr, G);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1259,77 +1327,29 @@ int mla_decode(const void* q, int32_t q_dtype, const void* q_scale, const void* 
   const int rc = mla_validate(q, q_dtype, q_scale, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch, page_table,
                               page_indptr, page_size, num_splits, out, workspace, workspace_bytes);
   if (rc != MLA_OK || batch == 0) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();  // clear a stale error so it is not misattributed
-  Stage1Args a;
-  a.q = q;
-  a.q_scale = q_scale;
-  a.kv = static_cast<const char*>(kv_cache);
-  a.kv_scale = kv_scale;
-  a.kv_indptr = kv_indptr;
-  a.page_table = page_table;
-  a.page_indptr = page_indptr;
-  const size_t parts = static_cast<size_t>(batch) * num_splits * kHeads;
-  a.part_o = num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  a.part_lse = num_splits > 1 ? static_cast<float*>(workspace) + parts * kDv : nullptr;
-  a.out = static_cast<uint16_t*>(out);
-  a.items = nullptr;
-  a.batch = batch;
-  a.page_size = page_size;
-  a.num_splits = num_splits;
-  a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);  // log2(e) / sqrt(576)
-  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(batch) * num_splits, st) != hipSuccess)
-    return MLA_ERR_LAUNCH;
-  if (num_splits > 1) {
-    hipLaunchKernelGGL(stage2_kernel, dim3(static_cast<unsigned>(batch) * 4), dim3(256), 0, st, a.part_o, a.part_lse,
-                       static_cast<uint16_t*>(out), num_splits, static_cast<const int32_t*>(nullptr));
-    if (hipGetLastError() != hipSuccess) return MLA_ERR_LAUNCH;
-  }
-  return MLA_OK;
+  return decode_launch(q, q_dtype, q_scale, kHeads, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch,
+                       page_table, page_indptr, page_size, num_splits, nullptr, 0, nullptr, 0, out, workspace,
+                       workspace_bytes, stream);
 }
 
-int mla_decode_worklist(const void* q, int32_t q_dtype, const void* q_scale, const void* kv_cache, int32_t kv_dtype,
-                        const void* kv_scale, int64_t num_kv_rows, const int32_t* kv_indptr, int32_t batch,
-                        const int32_t* page_table, const int32_t* page_indptr, int32_t page_size, const int32_t* items,
-                        int32_t num_items, const int32_t* req, int32_t num_slots, void* out, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  // the shared argument checks (one split: no workspace demanded here)
-  int rc = mla_validate(q, q_dtype, q_scale, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch, page_table,
-                        page_indptr, page_size, 1, out, nullptr, 0);
-  if (rc != MLA_OK || batch == 0) return rc;
-  if (!items || !req) return MLA_ERR_NULL;
-  if (num_items < batch || num_slots < 0) return MLA_ERR_ARG;
-  const size_t need = mla_worklist_workspace_bytes(num_slots);
-  if (need) {
-    if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return MLA_ERR_ALIGN;
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  Stage1Args a;
-  a.q = q;
-  a.q_scale = q_scale;
-  a.kv = static_cast<const char*>(kv_cache);
-  a.kv_scale = kv_scale;
-  a.kv_indptr = kv_indptr;
-  a.page_table = page_table;
-  a.page_indptr = page_indptr;
-  const size_t parts = static_cast<size_t>(num_slots) * kHeads;
-  a.part_o = num_slots > 0 ? static_cast<float*>(workspace) : nullptr;
-  a.part_lse = num_slots > 0 ? static_cast<float*>(workspace) + parts * kDv : nullptr;
-  a.out = static_cast<uint16_t*>(out);
-  a.items = items;
-  a.batch = batch;
-  a.page_size = page_size;
-  a.num_splits = 1;
-  a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);
-  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(num_items), st) != hipSuccess) return MLA_ERR_LAUNCH;
-  if (num_slots > 0) {
-    hipLaunchKernelGGL(stage2_kernel, dim3(static_cast<unsigned>(batch) * 4), dim3(256), 0, st, a.part_o, a.part_lse,
-                       static_cast<uint16_t*>(out), 1, req);
-    if (hipGetLastError() != hipSuccess) return MLA_ERR_LAUNCH;
-  }
-  return MLA_OK;
+int mla_decode_rows(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows, const void* kv_cache,
+                    int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows, const int32_t* kv_indptr,
+                    int32_t batch, const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                    int32_t num_splits, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_launch(q, q_dtype, q_scale, q_rows, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch,
+                       page_table, page_indptr, page_size, num_splits, nullptr, 0, nullptr, 0, out, workspace,
+                       workspace_bytes, stream);
+}
+
+int mla_decode_worklist(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows, const void* kv_cache,
+                        int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows, const int32_t* kv_indptr,
+                        int32_t batch, const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                        const int32_t* items, int32_t num_items, const int32_t* req, int32_t num_slots, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch > 0 && !items) return MLA_ERR_NULL;
+  return decode_launch(q, q_dtype, q_scale, q_rows, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch,
+                       page_table, page_indptr, page_size, 1, items, num_items, req, num_slots, out, workspace,
+                       workspace_bytes, stream);
 }
 
 int mla_quantize_fp8(const void* src_bf16, int64_t n, uint8_t* dst, float* scale, int32_t dynamic, void* stream) {

@@ -59,6 +59,12 @@ const char* mla_status_string(int status) {
   }
 }
 
+size_t mla_workspace_bytes_rows(int32_t batch, int32_t q_rows, int32_t num_splits) {
+  if (q_rows < MLA_NUM_HEADS || q_rows % MLA_NUM_HEADS || q_rows > MLA_MAX_Q_ROWS) return 0;
+  const size_t per16 = mla_workspace_bytes(batch, num_splits);
+  return per16 / MLA_NUM_HEADS * q_rows;
+}
+
 size_t mla_workspace_bytes(int32_t batch, int32_t num_splits) {
   if (batch < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return 0;
   if (num_splits == 1) return 0;
@@ -198,9 +204,9 @@ int mla_plan_worklist(const int32_t* kv_indptr_host, int32_t batch, int32_t num_
   return MLA_OK;
 }
 
-size_t mla_worklist_workspace_bytes(int32_t num_slots) {
-  if (num_slots <= 0) return 0;
-  const size_t parts = static_cast<size_t>(num_slots) * MLA_NUM_HEADS;
+size_t mla_worklist_workspace_bytes(int32_t num_slots, int32_t q_rows) {
+  if (num_slots <= 0 || q_rows < MLA_NUM_HEADS || q_rows % MLA_NUM_HEADS || q_rows > MLA_MAX_Q_ROWS) return 0;
+  const size_t parts = static_cast<size_t>(num_slots) * q_rows;
   return parts * MLA_HEAD_DIM_V * sizeof(float) + parts * sizeof(float);
 }
 

@@ -115,12 +115,12 @@ def prepare(case, q_fmt, kv_fmt, orc, q_static=6.0 / 448.0):
         assert np.array_equal(u8(g["q"]), codes)
         o.update(q=codes, q_dtype="fp8", q_scale=sc)
     else:
-        B = q_g.shape[0]
-        p, s = mla.quantize_mxfp4(q_g.reshape(B * 16, 576))
-        g["q"], g["q_scale"] = p.reshape(B, 16, 288), s
-        packed, e8 = orc.quant_mxfp4(bits(case["q"]).reshape(B * 16, 576))
+        B, R = q_g.shape[0], q_g.shape[1]
+        p, s = mla.quantize_mxfp4(q_g.reshape(B * R, 576))
+        g["q"], g["q_scale"] = p.reshape(B, R, 288), s
+        packed, e8 = orc.quant_mxfp4(bits(case["q"]).reshape(B * R, 576))
         assert np.array_equal(u8(p), packed) and np.array_equal(u8(s), e8)
-        o.update(q=packed.reshape(B, 16, 288), q_dtype="mxfp4", q_e8m0=e8)
+        o.update(q=packed.reshape(B, R, 288), q_dtype="mxfp4", q_e8m0=e8)
     return g, o
 
 
@@ -292,6 +292,36 @@ def test_worklist_per_request_pages(orc):
     torch.cuda.synchronize()
     ref, _ = oracle_decode(case, o, orc)
     check_close(out, ref, what="work list, per-request pages")
+
+
+@pytest.mark.parametrize("qf,kf", PAIRS)
+@pytest.mark.parametrize("rows,S", [(64, 1), (64, 3), (32, 2), (128, 1)])
+def test_multi_row_decode(orc, qf, kf, rows, S):
+    """q_seq_len x heads query rows per request (64 = 4 tokens x 16 heads,
+    32 / 128 = more heads), every row over the request's whole cache."""
+    lengths = [300, 1, 0, 777]
+    case = synth.make_case(len(lengths), lengths, 8, shuffle=True, seed=850 + rows)
+    case["q"] = synth.normal_bf16((len(lengths), rows, 576), seed=851 + rows)
+    g, o = prepare(case, qf, kf, orc)
+    out = gpu_decode(case, g, S)
+    assert out.shape == (len(lengths), rows, 512)
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what=f"{rows} rows {qf}/{kf} S={S}")
+    assert torch.all(out[2] == 0)
+
+
+def test_multi_row_worklist(orc):
+    lengths = [2500, 40, 0, 900]
+    case = synth.make_case(len(lengths), lengths, 8, shuffle=True, seed=860)
+    case["q"] = synth.normal_bf16((len(lengths), 64, 576), seed=861)
+    g, o = prepare(case, "bf16", "fp8", orc)
+    items, req, ns = mla.plan_worklist(case["kv_indptr"].cpu(), num_cus=16)
+    assert ns > 0
+    out = mla.decode_worklist(g["q"], g["kv"], g["kv_indptr"], g["page_table"], case["page_size"], items.to(DEV),
+                              req.to(DEV), ns, kv_scale=g["kv_scale"])
+    torch.cuda.synchronize()
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what="64 rows, work list")
 
 
 @pytest.mark.parametrize("S", [1, 4])

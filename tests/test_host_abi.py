@@ -206,5 +206,15 @@ def test_worklist_planner_limits(lib):
         mla.plan_worklist(np.array([0, 5, 3], dtype=np.int32))  # decreasing offsets
     items, req, ns = mla.plan_worklist(np.array([0], dtype=np.int32))
     assert len(items) == 0 and ns == 0
-    assert lib.mla_worklist_workspace_bytes(0) == 0
-    assert lib.mla_worklist_workspace_bytes(3) == 3 * 16 * 513 * 4
+    assert lib.mla_worklist_workspace_bytes(0, 16) == 0
+    assert lib.mla_worklist_workspace_bytes(3, 16) == 3 * 16 * 513 * 4
+    assert lib.mla_worklist_workspace_bytes(3, 64) == 3 * 64 * 513 * 4
+    assert lib.mla_worklist_workspace_bytes(3, 24) == 0  # not a multiple of 16
+
+
+def test_rows_workspace_bytes(lib):
+    for b, s in ((4, 1), (32, 8), (7, 3)):
+        assert lib.mla_workspace_bytes_rows(b, 16, s) == lib.mla_workspace_bytes(b, s)
+        assert lib.mla_workspace_bytes_rows(b, 64, s) == 4 * lib.mla_workspace_bytes(b, s)
+    assert lib.mla_workspace_bytes_rows(4, 8, 2) == 0
+    assert lib.mla_workspace_bytes_rows(4, 2048, 2) == 0
