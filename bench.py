@@ -344,6 +344,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=list(synth.WORKLOADS))
     ap.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-only", choices=["ragged", "multi_token"], default=None,
+                    help="time only this extra workload (for profiling) and print its JSON")
     ap.add_argument("--warmup-seconds", type=float, default=0.3,
                     help="minimum warm-up time per workload (0 for short profiled runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -372,6 +374,10 @@ def main():
         dt = (time.perf_counter() - t0) / args.steps
         print(json.dumps({"metric": "device copy", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
                           "us_per_copy": round(dt * 1e6, 2), "gbs": round(2 * src.numel() * 4 / dt / 1e9, 1)}))
+        return
+    if args.extra_only:
+        fn = time_ragged if args.extra_only == "ragged" else time_multi_token
+        print(json.dumps(fn(args.steps, args.warmup, device, args.warmup_seconds)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
     print(f"[bench] headline {w.name}", file=sys.stderr, flush=True)

@@ -324,6 +324,7 @@ struct Stage1Args {
   const int32_t* items;  // work-list plan (int32[num_items][4]), or NULL: split grid
   int32_t batch;
   int32_t groups;        // 16-row query groups per request (q_seq_len x heads / 16)
+  int32_t units;         // (request, split) pairs or work items
   int32_t page_size;
   int32_t num_splits;
   float sm_scale_log2e;
@@ -365,13 +366,23 @@ void stage1_kernel(Stage1Args a) {
   const int S = a.num_splits;
   // work decomposition: workgroup = (request, split) of a uniform split grid,
   // or one item {request, first token, tokens, slot} of a work-list plan,
-  // times the request's G 16-row query groups (the fastest index, so the
-  // workgroups sharing a token range are dispatched together and re-read it
-  // from cache)
+  // times the request's G 16-row query groups.  Workgroups are dealt to the
+  // eight XCDs round-robin by index, so with G > 1 the G groups of a unit
+  // get indices congruent mod 8: they run on one XCD, close together, and
+  // re-read the unit's tokens from that XCD's L2.  The grid is padded to a
+  // multiple of 8G; padding workgroups leave at once.
   const int G = a.groups;
   int b, s = 0, slot = -1, it_t0 = 0, it_n = 0;
-  const int unit = blockIdx.x / G;
-  const int r = blockIdx.x - unit * G;
+  int unit, r;
+  if (G == 1) {
+    unit = blockIdx.x;
+    r = 0;
+  } else {
+    const int k = blockIdx.x >> 3;
+    unit = 8 * (k / G) + (blockIdx.x & 7);
+    r = k - (k / G) * G;
+    if (unit >= a.units) return;
+  }
   if (a.items) {
     const int32_t* it = a.items + 4 * unit;
     b = min(max(it[0], 0), a.batch - 1);
@@ -1279,7 +1290,7 @@ int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q
   if (items && (!req)) return MLA_ERR_NULL;
   if (items && (num_items < batch || num_slots < 0)) return MLA_ERR_ARG;
   const int64_t units = items ? static_cast<int64_t>(num_items) : static_cast<int64_t>(batch) * num_splits;
-  if (units * G > 0x7fffffffLL || static_cast<int64_t>(batch) * G * 4 > 0x7fffffffLL) return MLA_ERR_ARG;
+  if ((units + 7) * G > 0x7fffffffLL || static_cast<int64_t>(batch) * G * 4 > 0x7fffffffLL) return MLA_ERR_ARG;
   const int64_t nslots = items ? num_slots : (num_splits > 1 ? static_cast<int64_t>(batch) * num_splits : 0);
   const size_t parts = static_cast<size_t>(nslots) * G * kHeads;
   const size_t need = parts * kDv * sizeof(float) + parts * sizeof(float);
@@ -1303,11 +1314,12 @@ int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q
   a.items = items;
   a.batch = batch;
   a.groups = G;
+  a.units = static_cast<int32_t>(units);
   a.page_size = page_size;
   a.num_splits = items ? 1 : num_splits;
   a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);  // log2(e) / sqrt(576)
-  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(units * G), st) != hipSuccess)
-    return MLA_ERR_LAUNCH;
+  const int64_t grid = G == 1 ? units : (units + 7) / 8 * 8 * G;
+  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(grid), st) != hipSuccess) return MLA_ERR_LAUNCH;
   if (need) {
     hipLaunchKernelGGL(stage2_kernel, dim3(static_cast<unsigned>(batch) * G * 4), dim3(256), 0, st, a.part_o,
                        a.part_lse, static_cast<uint16_t*>(out), items ? 1 : num_splits, items ? req : nullptr, G);
