@@ -454,3 +454,59 @@ def sampled_check(w, orc, n_req=6, seed_offset=0):
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_full_size_workload(orc, name):
     sampled_check(synth.WORKLOADS[name], orc)
+
+
+def _sampled_fp8_rows(orc, case, g, out, reqs, rows_of_q, what):
+    """Oracle over sampled requests (compacted to an identity page table) for an
+    fp8 cache with a bf16 Q of rows_of_q rows per request; checks rows 0, 5 and
+    the last one of each sampled request."""
+    P = case["page_size"]
+    pt = case["page_table"].cpu().numpy()
+    ind = case["kv_indptr"].cpu().numpy()
+    kv_sc = orc.fp8_scale_from_amax(orc.amax_bf16(bits(case["kv"])))
+    assert float(g["kv_scale"].item()) == kv_sc
+    for b in reqs:
+        L = int(ind[b + 1] - ind[b])
+        gpos = int(ind[b]) + np.arange(L)
+        rows = torch.from_numpy(pt[gpos // P].astype(np.int64) * P + gpos % P)
+        sub_kv = case["kv"][rows.to(DEV)].cpu()
+        codes, _ = orc.quant_fp8(bits(sub_kv), kv_sc)
+        assert np.array_equal(codes, u8(g["kv"][rows.to(DEV)]))
+        sub = {"kv_indptr": torch.tensor([0, L], dtype=torch.int32), "page_table": torch.arange(max(L, 1), dtype=torch.int32),
+               "page_indptr": None, "page_size": 1}
+        o = {"q": bits(case["q"][b:b + 1].cpu()), "q_dtype": "bf16", "kv": codes, "kv_dtype": "fp8", "kv_scale": kv_sc}
+        sel = [0, 5, rows_of_q - 1]
+        ref, _ = oracle_decode(sub, o, orc, pairs=[(0, h) for h in sel])
+        for h in sel:
+            check_close(out[b, h], ref[0, h], what=f"{what} b={b} row={h}", l2=1e-2)
+
+
+def test_full_size_ragged_worklist(orc):
+    """The ragged benchmark batch (64 lognormal lengths, total of bs=64
+    kv=8192) through the work list, as bench.py times it."""
+    print("[parity-full] ragged work list", flush=True)
+    lengths = synth.ragged_lengths(64, 8192, 1.0, synth.BASE_SEED + 50)
+    case = synth.make_case(64, lengths, 8, shuffle=True, seed=synth.BASE_SEED + 51, device=DEV)
+    g = {}
+    g["kv"], g["kv_scale"] = mla.quantize_fp8(case["kv"])
+    items, req, ns = mla.plan_worklist(case["kv_indptr"].cpu())
+    out = mla.decode_worklist(case["q"], g["kv"], case["kv_indptr"], case["page_table"], 8, items.to(DEV),
+                              req.to(DEV), ns, kv_scale=g["kv_scale"]).cpu()
+    longest = int(np.argmax(lengths))
+    reqs = sorted({0, 63, longest, int(np.argmin(lengths))})
+    _sampled_fp8_rows(orc, case, g, out, reqs, 16, "ragged")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_full_size_multi_token(orc):
+    """bs=64 kv=8192, 4 tokens x 16 heads (64 rows), as bench.py times it."""
+    print("[parity-full] multi-token", flush=True)
+    B, L, rows = 64, 8192, 64
+    case = synth.make_case(B, L, 8, shuffle=True, seed=synth.BASE_SEED + 60, device=DEV)
+    case["q"] = synth.normal_bf16((B, rows, 576), seed=synth.BASE_SEED + 61, device=DEV)
+    g = {}
+    g["kv"], g["kv_scale"] = mla.quantize_fp8(case["kv"])
+    S = mla.choose_num_splits(B * rows // 16, L, mla.FP8)
+    out = mla.decode(case["q"], g["kv"], case["kv_indptr"], case["page_table"], 8, S, kv_scale=g["kv_scale"]).cpu()
+    _sampled_fp8_rows(orc, case, g, out, [0, 17, 63], rows, "multi-token")
+    assert torch.isfinite(out.float()).all()
