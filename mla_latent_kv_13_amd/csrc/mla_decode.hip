@@ -1050,9 +1050,9 @@ void stage1_kernel(Stage1Args a) {
 // One workgroup per (request, group of 4 heads); a thread merges 8 columns of
 // one head over the S splits with base-2 log-sum-exp weights (empty splits,
 // LSE = -inf, are skipped; an all-empty request yields zeros).  One pass: the
-// LSEs and partial rows of eight splits are loaded together, and the running
-// maximum moves with a rescale of the accumulator (one load round trip for
-// S <= 8).
+// LSEs and partial rows of eight splits are loaded together, the next eight
+// are in flight while they are combined, and the running maximum moves with a
+// rescale of the accumulator.
 __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
                                                      uint16_t* __restrict__ out, int S, const int32_t* __restrict__ req,
                                                      int G) {
@@ -1077,36 +1077,52 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
   constexpr int kB = 8;
   float M = kNegInf, ws = 0.0f;
   f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += kB) {
-    float l[kB];
-    f32x4_t x0[kB], x1[kB];
+  // batch loads: splits [s0, s0 + kB), past the end a repeat weighted 0 below
+  float l[kB], ln[kB];
+  f32x4_t x0[kB], x1[kB], y0[kB], y1[kB];
+  auto load = [&](int s0, float* lb, f32x4_t* b0, f32x4_t* b1) {
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
-      const int si = min(s0 + i, S - 1);  // past the end: a repeat, weighted 0 below
-      l[i] = lse[si * stride];
-      x0[i] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv);
-      x1[i] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv + 4);
+      const int si = min(s0 + i, S - 1);
+      lb[i] = lse[si * stride];
+      b0[i] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv);
+      b1[i] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv + 4);
     }
+  };
+  load(0, l, x0, x1);
+  for (int s0 = 0; s0 < S; s0 += kB) {
+    // the next batch is in flight while this one is combined
+    const bool more = s0 + kB < S;
+    if (more) load(s0 + kB, ln, y0, y1);
 #pragma unroll
     for (int i = 0; i < kB; ++i)
       if (s0 + i >= S) l[i] = kNegInf;
     float mb = l[0];
 #pragma unroll
     for (int i = 1; i < kB; ++i) mb = fmax3(mb, l[i]);
-    if (mb == kNegInf) continue;  // every split of this batch is empty
-    const float Mn = fmax3(M, mb);
-    const float r = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-    a0 *= r;
-    a1 *= r;
-    ws *= r;
+    if (mb != kNegInf) {  // else every split of this batch is empty
+      const float Mn = fmax3(M, mb);
+      const float r = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+      a0 *= r;
+      a1 *= r;
+      ws *= r;
 #pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      const float wgt = l[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l[i] - Mn);
-      a0 += x0[i] * wgt;
-      a1 += x1[i] * wgt;
-      ws += wgt;
+      for (int i = 0; i < kB; ++i) {
+        const float wgt = l[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l[i] - Mn);
+        a0 += x0[i] * wgt;
+        a1 += x1[i] * wgt;
+        ws += wgt;
+      }
+      M = Mn;
     }
-    M = Mn;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        l[i] = ln[i];
+        x0[i] = y0[i];
+        x1[i] = y1[i];
+      }
+    }
   }
   const float inv = ws > 0.0f ? 1.0f / ws : 0.0f;
   a0 *= inv;
