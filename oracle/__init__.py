@@ -12,6 +12,7 @@ Parity status of each entry point (pins live in ``tests/test_oracle_*.py``):
   * codecs (bf16, e4m3fn, e2m1, e8m0)       pinned exhaustively
   * fp8 / mxfp4 quantisers                   pinned (library casts, worked cases, bounds)
   * decode (unsplit and split-wise)          pinned (library SDPA, closed forms, invariants)
+  * decode over a split cache (mxfp4 K, fp8 V) pinned (library SDPA, one-token and constant-key forms)
 """
 from __future__ import annotations
 
@@ -70,6 +71,9 @@ class _Problem(ctypes.Structure):
         ("page_table_len", ctypes.c_int64),
         ("page_size", ctypes.c_int32),
         ("rows", ctypes.c_int32),
+        ("v", ctypes.c_void_p),
+        ("v_dtype", ctypes.c_int32),
+        ("v_scale", ctypes.c_double),
     ]
 
 
@@ -196,13 +200,16 @@ def set_mutation(m: int) -> None:
 
 def decode(q, kv, kv_indptr, page_table, page_size, *, q_dtype="bf16", kv_dtype="bf16",
            q_scale=1.0, q_e8m0=None, kv_scale=1.0, kv_e8m0=None, page_indptr=None,
-           num_splits=0, pairs=None, nthreads=None):
+           num_splits=0, pairs=None, nthreads=None, v=None, v_dtype="fp8", v_scale=1.0):
     """fp64 MLA decode.
 
     q        : bf16 bits [B,rows,576] | e4m3fn codes [B,rows,576] | packed mxfp4 [B,rows,288]
                (rows = q_seq_len x heads query rows per request; 16 for
                single-token decode with 16 heads)
     kv       : physical rows, bf16 bits [R,576] | e4m3fn [R,576] | packed [R,288]
+    v        : optional value cache with the same physical rows, bf16 bits or
+               e4m3fn codes [R,576] (``v_dtype``, fp8 scale ``v_scale``); V is
+               then its dims 0..511 instead of the key rows'
     returns  : (out_f64 [B,rows,512], out_bf16_bits [B,rows,512]); rows of pairs not
                selected (when ``pairs`` is given) are NaN / 0.
     """
@@ -233,6 +240,17 @@ def decode(q, kv, kv_indptr, page_table, page_size, *, q_dtype="bf16", kv_dtype=
     P.page_size = int(page_size)
     rows = (qa.size // (B * (288 if qd == MXFP4 else 576))) if B > 0 else HEADS
     P.rows = rows
+    va = None
+    if v is not None:
+        vd = _DTYPES[v_dtype]
+        if vd == MXFP4:
+            raise ValueError("a separate value cache is bf16 or fp8")
+        va = _u16(v) if vd == BF16 else np.ascontiguousarray(v, dtype=np.uint8)
+        if va.shape[0] != ka.shape[0] or va.size != ka.shape[0] * D_QK:
+            raise ValueError("the value cache must hold the key cache's rows, 576 values each")
+        P.v = _ptr(va)
+        P.v_dtype = vd
+        P.v_scale = float(v_scale)
     out = np.full((B, rows, D_V), np.nan, dtype=np.float64)
     outb = np.zeros((B, rows, D_V), dtype=np.uint16)
     sel = None

@@ -34,6 +34,13 @@
  * request's own table starts at page_table[page_indptr[b]].  Its physical row
  * is page_table[first + g / P] * P + g % P.
  *
+ * Split cache (page 695854, its mxfp4 q=1 routes): the keys may come from
+ * one cache and the values from another holding the same tokens in the same
+ * physical rows - there the mxfp4 cache supplies all 576 key dims and the
+ * fp8 cache (with its per-tensor scale) the first 512 value dims.  With a
+ * separate value cache, v_t is that cache's dequantised row t, dims 0..511;
+ * otherwise it is k_hat_t[0:512] as above.
+ *
  * Split-wise variant (page 668813, the split-K stage 1 and its log2 combine;
  * page 600081, the split-K kernels): the token range of a request is cut into
  * S chunks of ceil(L/S) tokens; each non-empty chunk yields a normalised
@@ -74,7 +81,8 @@ enum { ORC_OK = 0, ORC_EARG = -1, ORC_EINDEX = -2, ORC_ENOMEM = -3 };
  *   1 drop the rope term from the logits     2 scale 1/sqrt(512) instead of 1/sqrt(576)
  *   3 read the next physical row             4 take V from dims 64..575
  *   5 use the neighbouring head's query      6 negate the logits
- *   7 swap the two nibbles of an mxfp4 byte  8 leave kv_scale off V          */
+ *   7 swap the two nibbles of an mxfp4 byte  8 leave kv_scale off V
+ *   9 take V from the key cache when a separate value cache is given      */
 static int g_mutation = 0;
 void orc_set_mutation(int m) { g_mutation = m; }
 
@@ -252,6 +260,9 @@ typedef struct {
   int64_t page_table_len;
   int32_t page_size;
   int32_t rows; /* query rows per request (q_seq_len x heads); 0 means 16 */
+  const void* v; /* optional value cache, same physical rows: bf16 | e4m3fn [R,576]; NULL = V from kv */
+  int32_t v_dtype;
+  double v_scale; /* fp8 value cache per-tensor scale */
 } orc_problem;
 
 static void deq_row(int dtype, const void* base, int64_t row, double scale, const uint8_t* e8m0, double* out) {
@@ -293,6 +304,7 @@ static int check_problem(const orc_problem* P) {
   if (P->q_dtype < 0 || P->q_dtype > 2 || P->kv_dtype < 0 || P->kv_dtype > 2) return ORC_EARG;
   if (P->q_dtype == ORC_MXFP4 && !P->q_e8m0) return ORC_EARG;
   if (P->kv_dtype == ORC_MXFP4 && !P->kv_e8m0) return ORC_EARG;
+  if (P->v && P->v_dtype != ORC_BF16 && P->v_dtype != ORC_FP8) return ORC_EARG;
   for (int b = 0; b < P->batch; b++)
     if (P->kv_indptr[b + 1] < P->kv_indptr[b]) return ORC_EARG;
   return ORC_OK;
@@ -341,7 +353,11 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
     const double inv_sqrt = (g_mutation == 6 ? -1.0 : 1.0) / sqrt(g_mutation == 2 ? 512.0 : (double)ORC_DQK);
     const int qk_dims = g_mutation == 1 ? ORC_DV : ORC_DQK;
     const int v0 = g_mutation == 4 ? 64 : 0;
-    const double v_fix = (g_mutation == 8 && P->kv_dtype == ORC_FP8) ? 1.0 / P->kv_scale : 1.0;
+    /* source of V: the separate value cache when one is given */
+    const int sep_v = P->v != NULL && g_mutation != 9;
+    const int v_dtype = sep_v ? P->v_dtype : P->kv_dtype;
+    const double v_scale = sep_v ? P->v_scale : P->kv_scale;
+    const double v_fix = (g_mutation == 8 && v_dtype == ORC_FP8) ? 1.0 / v_scale : 1.0;
     /* logits */
     for (int64_t t = 0; t < L && !bad; t++) {
       int64_t row = phys_row(P, b, t);
@@ -372,7 +388,10 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
           double p = exp(s[t] - m);
           l += p;
           int64_t row = phys_row(P, b, t);
-          deq_row(P->kv_dtype, P->kv, row, P->kv_scale, P->kv_e8m0, k);
+          if (sep_v)
+            deq_row(v_dtype, P->v, row, v_scale, NULL, k);
+          else
+            deq_row(P->kv_dtype, P->kv, row, P->kv_scale, P->kv_e8m0, k);
           for (int i = 0; i < ORC_DV; i++) os[(size_t)sp * ORC_DV + i] += p * k[v0 + i] * v_fix;
         }
         for (int i = 0; i < ORC_DV; i++) os[(size_t)sp * ORC_DV + i] /= l;

@@ -9,6 +9,10 @@
   exactly; permuting physical pages (with the table) changes nothing; a key
   planted as c*q dominates (one-hot probe of the gather).
 * Split-wise partial/merge form agrees with the unsplit softmax to 1e-12.
+* Split cache (keys from an mxfp4 cache, values from an fp8 cache of the same
+  rows): torch SDPA with separately dequantised K and V, one token gives that
+  token's fp8 value row exactly, and identical keys give the mean of the fp8
+  value rows.
 * Planted mistakes (oracle.c's mutation switch) each fail at least one pin.
 """
 import numpy as np
@@ -205,6 +209,58 @@ def pin_sdpa_multi_row(orc, fmt="fp8", rows=64):
     return out.shape == (3, rows, 512) and np.allclose(out, ref, rtol=1e-12, atol=1e-13)
 
 
+def mixed_case(orc, lengths, P, seed, shuffle=True):
+    """One logical cache in two physical forms on the same rows: mxfp4 keys
+    and fp8 values, with independent fp64 dequantisations of both."""
+    case = synth.make_case(len(lengths), lengths, P, shuffle=shuffle, seed=seed, extra_pages=2)
+    packed, kdeq_extra, kdeq = rows_f64(case, "mxfp4", orc)
+    codes, vextra, vdeq = rows_f64(case, "fp8", orc)
+    return case, packed, kdeq_extra["kv_e8m0"], kdeq, codes, vextra["kv_scale"], vdeq
+
+
+def run_mixed(orc, case, packed, e8, codes, vs, **kw):
+    return run(orc, case, packed, {"kv_e8m0": e8}, kv_dtype="mxfp4", v=codes, v_dtype="fp8", v_scale=vs, **kw)
+
+
+def pin_sdpa_mixed(orc):
+    case, packed, e8, kdeq, codes, vs, vdeq = mixed_case(orc, [17, 5, 9], 4, seed=29)
+    out, _ = run_mixed(orc, case, packed, e8, codes, vs)
+    q64 = case["q"].to(torch.float64).numpy()
+    ref = np.zeros((3, 16, 512))
+    for b in range(3):
+        L = case["lengths"][b]
+        rws = logical_rows(case, b, L)
+        kk = torch.from_numpy(kdeq[rws]).reshape(1, 1, L, 576).expand(1, 16, L, 576)
+        vv = torch.from_numpy(vdeq[rws, :512]).reshape(1, 1, L, 512).expand(1, 16, L, 512)
+        qq = torch.from_numpy(q64[b]).reshape(1, 16, 1, 576)
+        ref[b] = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv).reshape(16, 512).numpy()
+    return np.allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def pin_one_token_mixed(orc):
+    case, packed, e8, _, codes, vs, vdeq = mixed_case(orc, [1, 1], 1, seed=30)
+    out, _ = run_mixed(orc, case, packed, e8, codes, vs)
+    ok = True
+    for b in range(2):
+        row = logical_rows(case, b, 1)[0]
+        ok &= np.array_equal(out[b], np.broadcast_to(vdeq[row, :512], (16, 512)))
+    return ok
+
+
+def pin_constant_keys_mixed(orc):
+    # every key row the same: uniform weights whatever Q is, output = mean of
+    # the fp8 value rows
+    case, packed, e8, _, codes, vs, vdeq = mixed_case(orc, [7, 12], 3, seed=31)
+    packed = np.broadcast_to(packed[0], packed.shape).copy()
+    e8 = np.broadcast_to(e8[0], e8.shape).copy()
+    out, _ = run_mixed(orc, case, packed, e8, codes, vs)
+    ok = True
+    for b in range(2):
+        ref = vdeq[logical_rows(case, b, case["lengths"][b]), :512].mean(axis=0)
+        ok &= np.allclose(out[b], np.broadcast_to(ref, (16, 512)), rtol=1e-13, atol=1e-15)
+    return ok
+
+
 PINS = {
     "sdpa_bf16": lambda o: pin_sdpa(o, "bf16"),
     "sdpa_bf16_per_request_pages": lambda o: pin_sdpa(o, "bf16", per_request=True),
@@ -219,6 +275,9 @@ PINS = {
     "one_hot_probe": pin_one_hot_probe,
     "rope_shift": pin_rope_shift,
     "scale_fold": pin_scale_fold,
+    "sdpa_mixed": pin_sdpa_mixed,
+    "one_token_mixed": pin_one_token_mixed,
+    "constant_keys_mixed": pin_constant_keys_mixed,
 }
 
 
@@ -255,7 +314,7 @@ def test_selected_pairs_match_full(orc):
     assert np.isnan(part[0, 0]).all()
 
 
-@pytest.mark.parametrize("mutation", range(1, 9))
+@pytest.mark.parametrize("mutation", range(1, 10))
 def test_planted_mistake_fails_a_pin(orc, mutation):
     try:
         orc.set_mutation(mutation)
