@@ -279,6 +279,42 @@ def time_multi_token(steps, warmup, device, warmup_s=0.3):
     return res
 
 
+def time_mixed(steps, warmup, device, warmup_s=0.3):
+    """Split cache: bs=256, kv_len=8192, K from the mxfp4 cache and V from the
+    fp8 cache of the same rows (page 8, shuffled), mxfp4 Q as the pages'
+    mixed routes quantise it.  S = 2 (the mxfp4 benchmark shape's count) and
+    the heuristic's S.  Compulsory bytes: both caches' bytes actually read
+    (306 B of mxfp4 K and 512 B of fp8 V per token) + Q + page table + out."""
+    B, L, P = 256, 8192, 8
+    case = synth.make_case(B, L, P, shuffle=True, seed=synth.BASE_SEED + 70, device=device)
+    k, ks = mla.quantize_mxfp4(case["kv"])
+    v, vs = mla.quantize_fp8(case["kv"])
+    qp, qe = mla.quantize_mxfp4(case["q"].reshape(B * 16, 576))
+    q = qp.reshape(B, 16, 288)
+    ind, pt = case["kv_indptr"], case["page_table"]
+    del case
+    torch.cuda.empty_cache()
+    S_h = mla.choose_num_splits(B, L, mla.MIXED)
+    ws = torch.empty(max(16, mla.workspace_bytes(B, 2), mla.workspace_bytes(B, S_h)), dtype=torch.uint8,
+                     device=device)
+    out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=device)
+    ms2 = time_calls(lambda i: mla.decode_mixed(q, k, ks, v, vs, ind, pt, P, 2, q_scale=qe, out=out, workspace=ws),
+                     steps, warmup, warmup_s)[0]
+    msh = ms2 if S_h == 2 else time_calls(
+        lambda i: mla.decode_mixed(q, k, ks, v, vs, ind, pt, P, S_h, q_scale=qe, out=out, workspace=ws),
+        steps, warmup, warmup_s)[0]
+    T = B * L
+    nbytes = (306 + 512) * T + B * 16 * 306 + 4 * (T // P) + 4 * (B + 1) + B * 16 * 1024
+    res = {"workload": "bs256_kv8192_mxfp4k_fp8v_q4", "batch": B, "kv_len": L, "q": "mxfp4",
+           "kv": "mxfp4 K + fp8 V", "page_size": P, "num_splits": 2, "us_per_call": round(ms2 * 1e3, 3),
+           "gbs": round(nbytes / (ms2 * 1e-3) / 1e9, 1),
+           "frac_of_peak": round(nbytes / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "heuristic_num_splits": S_h, "us_heuristic_splits": round(msh * 1e3, 3), "compulsory_bytes": nbytes}
+    del k, v, q, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_ceiling(nbytes, device, steps=50):
     """Median GB/s of the library's streaming-read probe over a buffer of
     `nbytes` bytes: the practical HBM read ceiling for a read-once kernel."""
@@ -344,7 +380,7 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=list(synth.WORKLOADS))
     ap.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra-only", choices=["ragged", "multi_token"], default=None,
+    ap.add_argument("--extra-only", choices=["ragged", "multi_token", "mixed"], default=None,
                     help="time only this extra workload (for profiling) and print its JSON")
     ap.add_argument("--warmup-seconds", type=float, default=0.3,
                     help="minimum warm-up time per workload (0 for short profiled runs)")
@@ -376,7 +412,7 @@ def main():
                           "us_per_copy": round(dt * 1e6, 2), "gbs": round(2 * src.numel() * 4 / dt / 1e9, 1)}))
         return
     if args.extra_only:
-        fn = time_ragged if args.extra_only == "ragged" else time_multi_token
+        fn = {"ragged": time_ragged, "multi_token": time_multi_token, "mixed": time_mixed}[args.extra_only]
         print(json.dumps(fn(args.steps, args.warmup, device, args.warmup_seconds)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
@@ -395,6 +431,8 @@ def main():
         others.append(time_ragged(max(10, args.steps // 2), args.warmup, device, args.warmup_seconds))
         print("[bench] multi-token decode (64 query rows)", file=sys.stderr, flush=True)
         others.append(time_multi_token(max(10, args.steps // 2), args.warmup, device, args.warmup_seconds))
+        print("[bench] split cache (mxfp4 K, fp8 V)", file=sys.stderr, flush=True)
+        others.append(time_mixed(max(10, args.steps // 2), args.warmup, device, args.warmup_seconds))
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

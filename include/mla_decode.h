@@ -52,6 +52,9 @@ extern "C" {
 #define MLA_DTYPE_BF16 0         /* IEEE bfloat16 */
 #define MLA_DTYPE_FP8_E4M3FN 1   /* OCP fp8 e4m3fn with one fp32 per-tensor scale */
 #define MLA_DTYPE_MXFP4 2        /* OCP MX e2m1 + e8m0 per 32 elements */
+/* Split cache (mla_decode_mixed): K from an mxfp4 cache, V from an fp8 cache
+ * on the same rows.  Accepted as kv_dtype by mla_choose_num_splits only. */
+#define MLA_KV_MXFP4_K_FP8_V 3
 
 /* Status codes. */
 #define MLA_OK 0
@@ -222,6 +225,40 @@ int mla_decode_worklist(const void* q, int32_t q_dtype, const void* q_scale, int
                         const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
                         const int32_t* items, int32_t num_items, const int32_t* req, int32_t num_slots,
                         void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_mixed - decode over a split cache (page 695854, its triton and
+ * sage mxfp4 q=1 routes): the logits use the mxfp4 cache's keys (all 576
+ * dims) and the outputs the fp8 cache's values (dims 0..511 of its rows), the
+ * two caches holding the same tokens in the same physical rows:
+ *
+ *     out[b,h,:] = bf16( softmax_t( q[b,h,:] . kmx_t / sqrt(576) ) @ vfp8_t[0:512] )
+ *
+ * q, q_scale   bf16 [batch,q_rows,576] (q_dtype MLA_DTYPE_BF16, q_scale NULL)
+ *              or packed e2m1 [batch,q_rows,288] with e8m0 [batch*q_rows,18]
+ *              (MLA_DTYPE_MXFP4, as page 695854 quantises Q for these routes).
+ * k_cache      [num_kv_rows,288] packed e2m1, k_scale e8m0 [num_kv_rows,18]
+ *              (allocation padded as for mla_decode's mxfp4 kv_scale).
+ * v_cache      [num_kv_rows,576] e4m3fn (only bytes 0..511 of a row are
+ *              read), v_scale device float[1].
+ * The other arguments are as for mla_decode_rows (q_rows, paging, splits,
+ * workspace of mla_workspace_bytes_rows(batch, q_rows, num_splits)).  Errors
+ * as for mla_decode_rows; MLA_ERR_DTYPE for a q_dtype other than bf16 or
+ * mxfp4, MLA_ERR_NULL for a missing v_cache / v_scale, MLA_ERR_ALIGN for a
+ * v_cache that is not 16-byte or a v_scale that is not 4-byte aligned.
+ */
+int mla_decode_mixed(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows,
+                     const void* k_cache, const void* k_scale, const void* v_cache, const void* v_scale,
+                     int64_t num_kv_rows, const int32_t* kv_indptr, int32_t batch,
+                     const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                     int32_t num_splits, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The host-side argument checks of mla_decode_mixed (no HIP call). */
+int mla_validate_mixed(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows,
+                       const void* k_cache, const void* k_scale, const void* v_cache, const void* v_scale,
+                       int64_t num_kv_rows, const int32_t* kv_indptr, int32_t batch,
+                       const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                       int32_t num_splits, void* out, void* workspace, size_t workspace_bytes);
 
 /*
  * mla_quantize_fp8 - OCP e4m3fn per-tensor quantisation of n bf16 values

@@ -27,10 +27,11 @@ __all__ = [
     "BF16", "FP8", "MXFP4", "HEADS", "D_QK", "D_V",
     "load", "decode", "workspace_bytes", "choose_num_splits", "recommend_page_size",
     "quantize_fp8", "quantize_mxfp4", "validate", "status_string", "StatusError",
-    "mxfp4_scale_buffer",
+    "mxfp4_scale_buffer", "MIXED", "decode_mixed", "validate_mixed",
 ]
 
 BF16, FP8, MXFP4 = 0, 1, 2
+MIXED = 3  # split cache: mxfp4 K + fp8 V (format code for choose_num_splits)
 HEADS, D_QK, D_V = 16, 576, 512
 MXFP4_ROW_BYTES, MXFP4_ROW_SCALES = 288, 18
 MAX_SPLITS = 256
@@ -45,7 +46,7 @@ _DECODE_ARGS = [_c_void, _c_int32, _c_void, _c_void, _c_int32, _c_void, _c_int64
 EXPORTS = ("mla_decode", "mla_validate", "mla_workspace_bytes", "mla_choose_num_splits",
            "mla_recommend_page_size", "mla_quantize_fp8", "mla_quantize_mxfp4", "mla_stream_read",
            "mla_plan_worklist", "mla_worklist_workspace_bytes", "mla_decode_worklist", "mla_decode_rows",
-           "mla_workspace_bytes_rows",
+           "mla_workspace_bytes_rows", "mla_decode_mixed", "mla_validate_mixed",
            "mla_status_string", "mla_abi_version")
 
 
@@ -91,6 +92,12 @@ def load():
             L.mla_decode_rows.argtypes = _rows_args + [_c_int32, _c_void, _c_void, _c_size, _c_void]
             L.mla_workspace_bytes_rows.restype = _c_size
             L.mla_workspace_bytes_rows.argtypes = [_c_int32, _c_int32, _c_int32]
+            _mixed_args = [_c_void, _c_int32, _c_void, _c_int32, _c_void, _c_void, _c_void, _c_void, _c_int64,
+                           _c_void, _c_int32, _c_void, _c_void, _c_int32, _c_int32, _c_void, _c_void, _c_size]
+            L.mla_decode_mixed.restype = ctypes.c_int
+            L.mla_decode_mixed.argtypes = _mixed_args + [_c_void]
+            L.mla_validate_mixed.restype = ctypes.c_int
+            L.mla_validate_mixed.argtypes = _mixed_args
             L.mla_stream_read.restype = ctypes.c_int
             L.mla_stream_read.argtypes = [_c_void, _c_int64, _c_void, _c_void]
             L.mla_status_string.restype = ctypes.c_char_p
@@ -195,6 +202,60 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
         rc = L.mla_decode_rows(*args[:3], rows, *args[3:], _stream(stream))
     if rc:
         raise StatusError("mla_decode" if rows == HEADS else "mla_decode_rows", rc)
+    return out
+
+
+def _mixed_args(q, k_cache, k_scale, v_cache, v_scale, kv_indptr, page_table, page_size, num_splits, q_scale,
+                page_indptr, out, workspace):
+    batch = kv_indptr.numel() - 1
+    rows = _q_rows(q, batch)
+    num_rows = k_cache.shape[0] if k_cache.dim() else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return [_ptr(q), _fmt(q), _ptr(q_scale), rows, _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
+            num_rows, _ptr(kv_indptr), batch, _ptr(page_table), _ptr(page_indptr), int(page_size), int(num_splits),
+            _ptr(out), _ptr(workspace), ws_bytes]
+
+
+def validate_mixed(q, k_cache, k_scale, v_cache, v_scale, kv_indptr, page_table, page_size, num_splits, *,
+                   q_scale=None, page_indptr=None, out=None, workspace=None) -> int:
+    """Host-side argument check of decode_mixed (no GPU work); returns the status code."""
+    return int(load().mla_validate_mixed(*_mixed_args(q, k_cache, k_scale, v_cache, v_scale, kv_indptr, page_table,
+                                                      page_size, num_splits, q_scale, page_indptr, out, workspace)))
+
+
+def decode_mixed(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, v_cache: torch.Tensor,
+                 v_scale: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Tensor, page_size: int,
+                 num_splits: int | None = None, *, q_scale=None, page_indptr=None, out=None, workspace=None,
+                 kv_len_hint: int | None = None, stream=None):
+    """MLA decode over a split cache (mla_decode_mixed): logits from the mxfp4
+    keys, outputs from the fp8 values of the same rows.
+
+    q        [B,R,576] bf16, or [B,R,288] uint8 mxfp4 with q_scale e8m0 [B*R,18]
+    k_cache  [rows,288] uint8 packed e2m1, k_scale e8m0 [rows,18] (mxfp4_scale_buffer)
+    v_cache  [rows,576] float8_e4m3fn, v_scale 1-element float32 (only dims 0..511 are read)
+    Returns out [B,R,512] bf16 (enqueued on the current stream).
+    """
+    batch = kv_indptr.numel() - 1
+    rows = _q_rows(q, batch)
+    if num_splits is None:
+        hint = kv_len_hint if kv_len_hint is not None else max(1, k_cache.shape[0] // max(batch, 1))
+        num_splits = choose_num_splits(batch * (rows // HEADS), hint, MIXED)
+    if out is None:
+        out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=k_cache.device)
+    if workspace is None and batch > 0:
+        need = workspace_bytes(batch, num_splits, rows)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=k_cache.device)
+    _dev(q, k_cache, k_scale, v_cache, v_scale, kv_indptr, page_table, q_scale, page_indptr, out, workspace)
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.float8_e4m3fn:
+        raise TypeError("decode_mixed takes a uint8 mxfp4 key cache and a float8_e4m3fn value cache")
+    if v_cache.shape[0] != k_cache.shape[0]:
+        raise ValueError("the key and value caches must hold the same rows")
+    args = _mixed_args(q, k_cache, k_scale, v_cache, v_scale, kv_indptr, page_table, page_size, num_splits, q_scale,
+                       page_indptr, out, workspace)
+    rc = (_lib or load()).mla_decode_mixed(*args, _stream(stream))
+    if rc:
+        raise StatusError("mla_decode_mixed", rc)
     return out
 
 

@@ -29,6 +29,10 @@
 //     conversion plus register shuffles for mxfp4.
 //   * The four waves merge their (max, sum, O) through LDS at the end; S == 1
 //     writes bf16 out directly, otherwise fp32 partial O / base-2 LSE.
+//   * Split cache (page 695854's mxfp4 q=1 routes): K from the mxfp4 cache and
+//     V from the first 512 dims of an fp8 cache on the same rows.  Both rows
+//     of a token are staged into one slot; QK^T runs as for mxfp4 and P*V as
+//     for fp8.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -50,6 +54,7 @@ constexpr int kSub = 32;  // tokens per wave sub-tile
 constexpr int FBF16 = MLA_DTYPE_BF16;
 constexpr int FFP8 = MLA_DTYPE_FP8_E4M3FN;
 constexpr int FMX = MLA_DTYPE_MXFP4;
+constexpr int FMIX = MLA_KV_MXFP4_K_FP8_V;  // mxfp4 K + fp8 V, two caches
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -88,6 +93,19 @@ template <> struct Kv<FMX> {
   static constexpr int kNdmaSc = 3;  // 32 tokens x 5 aligned dwords = 160 lanes
   static constexpr int kNbuf = 3;
 };
+// Split cache: a slot holds the 32 tokens' mxfp4 K rows (18 units each, as
+// for mxfp4) followed by their fp8 V rows cut to the 512 value dims (32
+// units each); one slot per wave fits the LDS.
+template <> struct Kv<FMIX> {
+  static constexpr int kRow = MLA_MXFP4_ROW_BYTES;  // K cache row; V rows are 576 B
+  static constexpr int kUnitsK = kRow / 16;
+  static constexpr int kUnitsV = kDv / 16;
+  static constexpr int kUnits = kUnitsK + kUnitsV;
+  static constexpr int kNdmaK = kUnitsK / 2;
+  static constexpr int kNdmaX4 = kUnits / 2;
+  static constexpr int kNdmaSc = 3;
+  static constexpr int kNbuf = 1;
+};
 
 template <int KF> struct Lay {
   static constexpr int kNbuf = Kv<KF>::kNbuf;
@@ -102,7 +120,9 @@ template <int KF> struct Lay {
   static constexpr int kPidOff = kParOff + kNbuf * kParSlot;
   static constexpr int kRowOff = kPidOff + kNpid * kPidSlot;       // physical row per token (u32)
   static constexpr int kPtrOff = kRowOff + 4 * kSub;                // row base address per token (u64)
-  static constexpr int kWaveBytes = kPtrOff + 8 * kSub;
+  // split cache: the V rows' base addresses follow the K rows'
+  static constexpr int kPtrBytes = (KF == FMIX ? 2 : 1) * 8 * kSub;
+  static constexpr int kWaveBytes = kPtrOff + kPtrBytes;
   static constexpr int kCombine = kWaves * 32768 + 2 * kWaves * kHeads * 4;  // 4 partial O^T + (m, l)
   static constexpr int kTotal = kWaves * kWaveBytes > kCombine ? kWaves * kWaveBytes : kCombine;
   static constexpr int kNdma = Kv<KF>::kNdmaX4 + Kv<KF>::kNdmaSc;  // VMEM instrs per sub-tile
@@ -123,6 +143,11 @@ __device__ __forceinline__ int tswz(int t) {
   else if constexpr (KF == FBF16) return ((t >> 2) & 1) | (((t >> 1) & 1) << 1);
   else return 0;
 }
+// The split cache's V rows are 32 units (512 B) long, so every token's unit k
+// falls in the same bank group; flipping the three low unit bits with token
+// bits 0, 1 and 4 gives the eight tokens of one transposing-read phase
+// (4g..4g+3, 16+4g..16+4g+3) eight different groups.
+__device__ __forceinline__ int vswz(int t) { return (t & 3) | (((t >> 4) & 1) << 2); }
 
 // ------------------------------------------------------------- primitives
 template <class T>
@@ -315,6 +340,8 @@ struct Stage1Args {
   const void* q_scale;
   const char* kv;
   const void* kv_scale;
+  const char* kv2;        // split cache: fp8 V rows (576 B, dims 0..511 read), else NULL
+  const float* kv2_scale;  // split cache: the V cache's per-tensor scale
   const int32_t* kv_indptr;
   const int32_t* page_table;
   const int32_t* page_indptr;
@@ -337,6 +364,8 @@ template <> struct QFrag<FBF16, FFP8> { static constexpr int kN = 18; };
 template <> struct QFrag<FBF16, FMX> { static constexpr int kN = 5; };  // hi/lo fp8 pairs
 template <> struct QFrag<FFP8, FFP8> { static constexpr int kN = 5; };
 template <> struct QFrag<FMX, FMX> { static constexpr int kN = 5; };
+template <> struct QFrag<FBF16, FMIX> { static constexpr int kN = 5; };
+template <> struct QFrag<FMX, FMIX> { static constexpr int kN = 5; };
 
 // First latent dim of the 8 bf16 values that QK MFMA m takes from lane group g,
 // for bf16 Q (the permutation mirrors how the K operand is read from LDS).
@@ -405,7 +434,8 @@ void stage1_kernel(Stage1Args a) {
   // split costs a few microseconds per wave (the fp8 encoder is a slow
   // instruction), which only the long, compute-bound mxfp4 splits repay; over
   // the fp8 cache, K is widened to bf16 instead (full-rate converts).
-  constexpr bool kSplitQ = QF == FBF16 && KF == FMX;
+  constexpr bool kMxK = KF == FMX || KF == FMIX;  // K from an mxfp4 cache
+  constexpr bool kSplitQ = QF == FBF16 && kMxK;
   bf16x8_t qb[QF == FBF16 && !kSplitQ ? NQ : 1];
   u32x4_t qraw[kSplitQ ? 4 * NQ : 1];
   i32x8_t q8[QF == FFP8 || kSplitQ ? NQ : 1];
@@ -455,6 +485,8 @@ void stage1_kernel(Stage1Args a) {
     }
   }
   if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
+  float vs = 1.0f;  // split cache: V scale, applied with the final division
+  if constexpr (KF == FMIX) vs = *a.kv2_scale;
   const int kv0 = a.kv_indptr[b];
   const int Lr = a.kv_indptr[b + 1] - kv0;
   int t0, n;  // first token and token count of this workgroup's range
@@ -496,9 +528,24 @@ void stage1_kernel(Stage1Args a) {
   // bf16 (36) recomputes them from an opaque lane index instead.
   constexpr bool kPre = Kv<KF>::kNdmaX4 <= 36;
   auto dma_pack = [](int i, int ln) {
-    const int c = 64 * i + ln;
-    const int t = c / U;
-    return ((8 * t) << 16) | (16 * ((c - t * U) ^ tswz<KF>(t)));
+    if constexpr (KF == FMIX) {
+      // K rows: chunks 64i + ln of an 18-unit row-major stream; V rows: 32
+      // units each, unit k stored at k ^ vswz(t), addressed through the
+      // second row-pointer table
+      constexpr int UK = Kv<FMIX>::kUnitsK, NK = Kv<FMIX>::kNdmaK;
+      if (i < NK) {
+        const int c = 64 * i + ln;
+        const int t = c / UK;
+        return ((8 * t) << 16) | (16 * (c - t * UK));
+      }
+      const int c = 64 * (i - NK) + ln;
+      const int t = c >> 5;
+      return ((8 * kSub + 8 * t) << 16) | (16 * ((c & 31) ^ vswz(t)));
+    } else {
+      const int c = 64 * i + ln;
+      const int t = c / U;
+      return ((8 * t) << 16) | (16 * ((c - t * U) ^ tswz<KF>(t)));
+    }
   };
   int dmao[kPre ? Kv<KF>::kNdmaX4 : 1];
 #pragma unroll
@@ -541,7 +588,9 @@ void stage1_kernel(Stage1Args a) {
       const uint32_t row = pid * P + gpos % P;
       lds_st<uint32_t>(rt + 4 * lane, row);
       lds_st<uint64_t>(pt + 8 * lane, reinterpret_cast<uint64_t>(a.kv + static_cast<int64_t>(row) * ROW));
-      if constexpr (KF == FMX) lds_st<uint8_t>(static_cast<int>(par_addr(x)) + lane, static_cast<uint8_t>(row & 1));
+      if constexpr (KF == FMIX)
+        lds_st<uint64_t>(pt + 8 * kSub + 8 * lane, reinterpret_cast<uint64_t>(a.kv2 + static_cast<int64_t>(row) * kDqk));
+      if constexpr (kMxK) lds_st<uint8_t>(static_cast<int>(par_addr(x)) + lane, static_cast<uint8_t>(row & 1));
     }
     // Row-pointer reads in batches of up to 18 (one LDS latency per batch),
     // each batch followed by its DMA instructions.
@@ -559,20 +608,24 @@ void stage1_kernel(Stage1Args a) {
       }
 #pragma unroll
       for (int i0 = 0; i0 < Kv<KF>::kNdmaX4; i0 += NB) {
+        constexpr int NT = Kv<KF>::kNdmaX4;
         uint64_t rptr[NB];
         int off[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          if constexpr (kPre) off[i] = dmao[i0 + i];
-          else off[i] = dma_pack(i0 + i, lnv);
-          rptr[i] = lds_ld<uint64_t>(pt + (off[i] >> 16));
+          if (i0 + i < NT) {
+            if constexpr (kPre) off[i] = dmao[i0 + i];
+            else off[i] = dma_pack(i0 + i, lnv);
+            rptr[i] = lds_ld<uint64_t>(pt + (off[i] >> 16));
+          }
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-          dma_x4_nt(reinterpret_cast<const char*>(rptr[i]) + (off[i] & 0xffff), slot_addr(x) + 1024u * (i0 + i));
+          if (i0 + i < NT)
+            dma_x4_nt(reinterpret_cast<const char*>(rptr[i]) + (off[i] & 0xffff), slot_addr(x) + 1024u * (i0 + i));
       }
     };
-    if constexpr (KF == FMX) {
+    if constexpr (kMxK) {
       const uint8_t* ksc = static_cast<const uint8_t*>(a.kv_scale);
       const uint8_t* sp[3];
 #pragma unroll
@@ -598,7 +651,7 @@ void stage1_kernel(Stage1Args a) {
   }
 
   const float c_log2 = a.sm_scale_log2e * qs * ks;
-  const float out_mul = KF == FFP8 ? ks : 1.0f;
+  const float out_mul = KF == FFP8 ? ks : KF == FMIX ? vs : 1.0f;
   // Wait for the page ids and Q together, and make the compiler see Q as
   // complete here, so its own wait for Q cannot drain the in-flight tiles later.
   wait_vm<0>();
@@ -636,22 +689,30 @@ void stage1_kernel(Stage1Args a) {
     // fp8 V^T fragments for P*V, one transposing read per 16-column tile:
     // lane j of a 16-lane group addresses token T[j/2] (8 B at column 8*(j%2)),
     // T = {4g..4g+3, 16+4g..16+4g+3}; lane i then holds column i of all eight.
-    i32x2_t vv[KF == FFP8 ? 32 : 1];
+    constexpr bool kV8 = KF == FFP8 || KF == FMIX;  // fp8 V
+    i32x2_t vv[kV8 ? 32 : 1];
     const int tvj = (lane & 15) >> 1;
     const int tv8 = tvj < 4 ? 4 * g + tvj : 16 + 4 * g + (tvj - 4);
-    // unit c of token tv8 sits at chunk 4(c>>2) + ((c&3) ^ tswz): four lane
-    // bases, the rest is an immediate offset
-    int vb[4];
+    // unit c of token tv8 sits at chunk NVB(c / NVB) + ((c % NVB) ^ swizzle):
+    // NVB lane bases (the swizzle flips the log2(NVB) low bits), the rest is
+    // an immediate offset.  The split cache's V rows start after the K rows.
+    constexpr int NVB = KF == FMIX ? 8 : 4;
+    constexpr int UV = KF == FMIX ? Kv<FMIX>::kUnitsV : U;
+    const int tbv = KF == FMIX ? tb + kSub * Kv<FMIX>::kUnitsK * 16 : tb;
+    const int vsw = KF == FMIX ? vswz(tv8) : tswz<KF>(tv8);
+    int vb[NVB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vb[r] = tb + 16 * (tv8 * U + (r ^ tswz<KF>(tv8))) + 8 * (lane & 1);
+    for (int r = 0; r < NVB; ++r) vb[r] = tbv + 16 * (tv8 * UV + (r ^ vsw)) + 8 * (lane & 1);
     auto tr8_frag = [&](int c) {
       return __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<__attribute__((address_space(3))) i32x2_t*>(
-          static_cast<uintptr_t>(vb[c & 3] + 64 * (c >> 2))));
+          static_cast<uintptr_t>(vb[c % NVB] + 16 * NVB * (c / NVB))));
     };
     // QK fragment of token t, unit 4c + g (any unit index of that form keeps
-    // the swizzle inside its low two bits)
-    const int qb0 = tb + 16 * (tq0 * U + (g ^ tswz<KF>(tq0)));
-    const int qb1 = tb + 16 * (tq1 * U + (g ^ tswz<KF>(tq1)));
+    // the swizzle inside its low two bits); the split cache's K rows are
+    // mxfp4 rows of 18 units
+    constexpr int UK = KF == FMIX ? Kv<FMIX>::kUnitsK : U;
+    const int qb0 = tb + 16 * (tq0 * UK + (g ^ tswz<KF>(tq0)));
+    const int qb1 = tb + 16 * (tq1 * UK + (g ^ tswz<KF>(tq1)));
     auto qoff = [&](int t, int c) { return (t == tq0 ? qb0 : qb1) + 64 * c; };
     // ---------------- QK^T: both 16-token tiles at once (two independent
     // accumulator chains), every LDS fragment fetched before the MFMAs run.
@@ -746,8 +807,8 @@ void stage1_kernel(Stage1Args a) {
         c0[4] = 127u;
         c1[4] = 127u;
         if (g < 2) {
-          u0[4] = lds_ld<i32x4_t>(tb + 16 * (tq0 * U + 16 + g));
-          u1[4] = lds_ld<i32x4_t>(tb + 16 * (tq1 * U + 16 + g));
+          u0[4] = lds_ld<i32x4_t>(tb + 16 * (tq0 * UK + 16 + g));
+          u1[4] = lds_ld<i32x4_t>(tb + 16 * (tq1 * UK + 16 + g));
           c0[4] = lds_ld<uint8_t>(sb0 + 16 + g);
           c1[4] = lds_ld<uint8_t>(sb1 + 16 + g);
         }
@@ -852,7 +913,7 @@ void stage1_kernel(Stage1Args a) {
           acc[8 * cg + e] = mfma_bf16(av, pb, acc[8 * cg + e]);
         }
       }
-    } else if constexpr (KF == FFP8) {
+    } else if constexpr (kV8) {
       // four groups of eight 16-column tiles, two groups of reads in flight
 #pragma unroll
       for (int c = 0; c < 16; ++c) vv[c] = tr8_frag(c);
@@ -1255,6 +1316,8 @@ hipError_t launch_stage1_any(const Stage1Args& a, int32_t q_dtype, int32_t kv_dt
   if (kv_dtype == MLA_DTYPE_BF16) return launch_stage1<FBF16, FBF16>(a, grid, st);
   if (kv_dtype == MLA_DTYPE_FP8_E4M3FN)
     return q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FFP8>(a, grid, st) : launch_stage1<FFP8, FFP8>(a, grid, st);
+  if (kv_dtype == MLA_KV_MXFP4_K_FP8_V)
+    return q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FMIX>(a, grid, st) : launch_stage1<FMX, FMIX>(a, grid, st);
   return q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FMX>(a, grid, st) : launch_stage1<FMX, FMX>(a, grid, st);
 }
 
@@ -1290,17 +1353,24 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
 }
 
 // Shared launcher: uniform splits (items == NULL) or a work-list plan, for
-// q_rows query rows per request (G = q_rows / 16 query groups).
+// q_rows query rows per request (G = q_rows / 16 query groups).  kv_dtype
+// MLA_KV_MXFP4_K_FP8_V is the split cache: kv_cache / kv_scale are its mxfp4
+// K side, v_cache / v_scale its fp8 V side (otherwise both NULL).
 int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows, const void* kv_cache,
                   int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows, const int32_t* kv_indptr,
                   int32_t batch, const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
                   int32_t num_splits, const int32_t* items, int32_t num_items, const int32_t* req, int32_t num_slots,
-                  void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                  void* out, void* workspace, size_t workspace_bytes, void* stream, const void* v_cache = nullptr,
+                  const void* v_scale = nullptr) {
   if (q_rows < kHeads || q_rows % kHeads || q_rows > MLA_MAX_Q_ROWS) return MLA_ERR_ARG;
   const int G = q_rows / kHeads;
   // the shared argument checks, without the workspace (sized per mode below)
-  int rc = mla_validate(q, q_dtype, q_scale, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch, page_table,
-                        page_indptr, page_size, items ? 1 : num_splits, out, nullptr, 0);
+  const bool mixed = kv_dtype == MLA_KV_MXFP4_K_FP8_V;
+  int rc = mixed ? mla_validate_mixed(q, q_dtype, q_scale, q_rows, kv_cache, kv_scale, v_cache, v_scale, num_kv_rows,
+                                      kv_indptr, batch, page_table, page_indptr, page_size,
+                                      items ? 1 : num_splits, out, nullptr, 0)
+                 : mla_validate(q, q_dtype, q_scale, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch,
+                                page_table, page_indptr, page_size, items ? 1 : num_splits, out, nullptr, 0);
   if (rc == MLA_ERR_WORKSPACE) rc = MLA_OK;  // checked below
   if (rc != MLA_OK || batch == 0) return rc;
   if (items && (!req)) return MLA_ERR_NULL;
@@ -1321,6 +1391,8 @@ int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q
   a.q_scale = q_scale;
   a.kv = static_cast<const char*>(kv_cache);
   a.kv_scale = kv_scale;
+  a.kv2 = static_cast<const char*>(v_cache);
+  a.kv2_scale = static_cast<const float*>(v_scale);
   a.kv_indptr = kv_indptr;
   a.page_table = page_table;
   a.page_indptr = page_indptr;
@@ -1378,6 +1450,16 @@ int mla_decode_worklist(const void* q, int32_t q_dtype, const void* q_scale, int
   return decode_launch(q, q_dtype, q_scale, q_rows, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch,
                        page_table, page_indptr, page_size, 1, items, num_items, req, num_slots, out, workspace,
                        workspace_bytes, stream);
+}
+
+int mla_decode_mixed(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows, const void* k_cache,
+                     const void* k_scale, const void* v_cache, const void* v_scale, int64_t num_kv_rows,
+                     const int32_t* kv_indptr, int32_t batch, const int32_t* page_table, const int32_t* page_indptr,
+                     int32_t page_size, int32_t num_splits, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return decode_launch(q, q_dtype, q_scale, q_rows, k_cache, MLA_KV_MXFP4_K_FP8_V, k_scale, num_kv_rows, kv_indptr,
+                       batch, page_table, page_indptr, page_size, num_splits, nullptr, 0, nullptr, 0, out, workspace,
+                       workspace_bytes, stream, v_cache, v_scale);
 }
 
 int mla_quantize_fp8(const void* src_bf16, int64_t n, uint8_t* dst, float* scale, int32_t dynamic, void* stream) {

@@ -23,6 +23,7 @@ int64_t kv_row_bytes(int32_t kd) {
   switch (kd) {
     case MLA_DTYPE_BF16: return 2 * MLA_HEAD_DIM_QK;
     case MLA_DTYPE_FP8_E4M3FN: return MLA_HEAD_DIM_QK;
+    case MLA_KV_MXFP4_K_FP8_V: return MLA_MXFP4_ROW_BYTES + MLA_MXFP4_ROW_SCALES + MLA_HEAD_DIM_V;
     default: return MLA_MXFP4_ROW_BYTES + MLA_MXFP4_ROW_SCALES;
   }
 }
@@ -101,10 +102,32 @@ int mla_validate(const void* q, int32_t q_dtype, const void* q_scale, const void
   return MLA_OK;
 }
 
+int mla_validate_mixed(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows, const void* k_cache,
+                       const void* k_scale, const void* v_cache, const void* v_scale, int64_t num_kv_rows,
+                       const int32_t* kv_indptr, int32_t batch, const int32_t* page_table,
+                       const int32_t* page_indptr, int32_t page_size, int32_t num_splits, void* out,
+                       void* workspace, size_t workspace_bytes) {
+  if (q_rows < MLA_NUM_HEADS || q_rows % MLA_NUM_HEADS || q_rows > MLA_MAX_Q_ROWS) return MLA_ERR_ARG;
+  // the K side is an mxfp4 cache in every respect; its workspace check is
+  // for 16 rows, so it is redone below for q_rows
+  int rc = mla_validate(q, q_dtype, q_scale, k_cache, MLA_DTYPE_MXFP4, k_scale, num_kv_rows, kv_indptr, batch,
+                        page_table, page_indptr, page_size, num_splits, out, nullptr, 0);
+  if (rc == MLA_ERR_WORKSPACE) rc = MLA_OK;
+  if (rc != MLA_OK || batch == 0) return rc;
+  if (!v_cache || !v_scale) return MLA_ERR_NULL;
+  if (!aligned16(v_cache) || (reinterpret_cast<uintptr_t>(v_scale) & 3u)) return MLA_ERR_ALIGN;
+  const size_t need = mla_workspace_bytes_rows(batch, q_rows, num_splits);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  }
+  return MLA_OK;
+}
+
 int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, int32_t num_cus) {
   if (batch < 1 || kv_len < 1) return 1;
   if (num_cus <= 0) num_cus = 256;
-  if (kv_dtype < MLA_DTYPE_BF16 || kv_dtype > MLA_DTYPE_MXFP4) kv_dtype = MLA_DTYPE_FP8_E4M3FN;
+  if (kv_dtype < MLA_DTYPE_BF16 || kv_dtype > MLA_KV_MXFP4_K_FP8_V) kv_dtype = MLA_DTYPE_FP8_E4M3FN;
   // Shapes of the tuned grid (MI355X, 256 CUs) take the measured optimum.
   if (num_cus == 256) {
     for (const SplitEntry& e : kSplitTable)

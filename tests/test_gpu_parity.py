@@ -510,3 +510,132 @@ def test_full_size_multi_token(orc):
     out = mla.decode(case["q"], g["kv"], case["kv_indptr"], case["page_table"], 8, S, kv_scale=g["kv_scale"]).cpu()
     _sampled_fp8_rows(orc, case, g, out, [0, 17, 63], rows, "multi-token")
     assert torch.isfinite(out.float()).all()
+
+
+# ------------------------------------------------- split cache (mxfp4 K, fp8 V)
+def prepare_mixed(case, q_fmt, orc, v_seed=None):
+    """mxfp4 key cache from case["kv"] and an fp8 value cache on the same rows,
+    from case["kv"] or (v_seed) from independent N(0,1) data, so that a kernel
+    reading V from the wrong cache cannot pass.  GPU and oracle quantisers
+    must agree bit for bit."""
+    g, o = prepare(case, q_fmt, "mxfp4", orc)
+    vsrc = case["kv"] if v_seed is None else synth.normal_bf16(tuple(case["kv"].shape), seed=v_seed)
+    g["v"], g["v_scale"] = mla.quantize_fp8(vsrc.to(DEV))
+    codes, sc = orc.quant_fp8(bits(vsrc))
+    assert float(g["v_scale"].item()) == sc and np.array_equal(u8(g["v"]), codes)
+    o.update(v=codes, v_scale=sc)
+    return g, o, vsrc
+
+
+def gpu_decode_mixed(case, g, S):
+    out = mla.decode_mixed(g["q"], g["kv"], g["kv_scale"], g["v"], g["v_scale"], g["kv_indptr"], g["page_table"],
+                           case["page_size"], S, q_scale=g["q_scale"], page_indptr=g["page_indptr"])
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_mixed(case, o, orc, pairs=None):
+    return orc.decode(o["q"], o["kv"], case["kv_indptr"].cpu().numpy(), case["page_table"].cpu().numpy(),
+                      case["page_size"], q_dtype=o["q_dtype"], kv_dtype="mxfp4", q_e8m0=o.get("q_e8m0"),
+                      kv_e8m0=o["kv_e8m0"], v=o["v"], v_dtype="fp8", v_scale=o["v_scale"],
+                      page_indptr=None if case["page_indptr"] is None else case["page_indptr"].cpu().numpy(),
+                      pairs=pairs)
+
+
+@pytest.mark.parametrize("qf", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+def test_mixed_matches_oracle(orc, qf, shape):
+    lengths, P, S, per_req = SHAPES[shape]
+    print(f"[parity-mixed] q={qf} lengths={lengths} P={P} S={S} per_request={per_req}", flush=True)
+    case = synth.make_case(len(lengths), lengths, P, shuffle=True, seed=900 + shape, per_request_pages=per_req,
+                           extra_pages=2)
+    g, o, _ = prepare_mixed(case, qf, orc, v_seed=950 + shape)
+    out = gpu_decode_mixed(case, g, S)
+    ref, _ = oracle_mixed(case, o, orc)
+    check_close(out, ref, what=f"mixed {qf} shape {shape}")
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert not out[b].any()
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 8, 32, 256])
+def test_mixed_split_count_invariance(orc, S):
+    case = synth.make_case(3, [700, 129, 1], 8, shuffle=True, seed=960)
+    g, o, _ = prepare_mixed(case, "mxfp4", orc, v_seed=961)
+    ref, _ = oracle_mixed(case, o, orc)
+    check_close(gpu_decode_mixed(case, g, S), ref, what=f"mixed S={S}")
+
+
+def test_mixed_one_token_is_its_value_row(orc):
+    """One token per request: the output is that token's fp8 value row, to
+    within one bf16 rounding (the kernel's fp32 p*v/p may move a value that
+    sits on a rounding boundary by one bf16 step)."""
+    case = synth.make_case(3, [1, 1, 1], 2, shuffle=True, seed=962)
+    g, o, _ = prepare_mixed(case, "bf16", orc, v_seed=963)
+    out = gpu_decode_mixed(case, g, 1)
+    ref, _ = oracle_mixed(case, o, orc)
+    check_close(out, ref, atol=1e-30, rtol=2.0 ** -7, l2=None, what="one token, split cache")
+
+
+@pytest.mark.parametrize("rows,S", [(64, 1), (32, 3)])
+def test_mixed_multi_row(orc, rows, S):
+    lengths = [300, 1, 0, 777]
+    case = synth.make_case(len(lengths), lengths, 8, shuffle=True, seed=970 + rows)
+    case["q"] = synth.normal_bf16((len(lengths), rows, 576), seed=971 + rows)
+    g, o, _ = prepare_mixed(case, "mxfp4", orc, v_seed=972 + rows)
+    out = gpu_decode_mixed(case, g, S)
+    assert out.shape == (len(lengths), rows, 512)
+    ref, _ = oracle_mixed(case, o, orc)
+    check_close(out, ref, what=f"mixed {rows} rows S={S}")
+    assert torch.all(out[2] == 0)
+
+
+def test_mixed_invalid_arguments_raise(orc):
+    case = synth.make_case(2, [40, 9], 1, shuffle=False, seed=980)
+    g, _, _ = prepare_mixed(case, "bf16", orc)
+    qf8, qs = mla.quantize_fp8(g["q"], 0.01)
+    with pytest.raises(mla.StatusError):   # fp8 Q is not a split-cache pair
+        mla.decode_mixed(qf8, g["kv"], g["kv_scale"], g["v"], g["v_scale"], g["kv_indptr"], g["page_table"], 1, 1,
+                         q_scale=qs)
+    with pytest.raises(TypeError):
+        mla.decode_mixed(g["q"], g["kv"], g["kv_scale"], g["v"].view(torch.uint8), g["v_scale"], g["kv_indptr"],
+                         g["page_table"], 1, 1)
+
+
+def test_full_size_mixed(orc):
+    """bs=256 kv=8192 over the split cache (mxfp4 Q, mxfp4 K, fp8 V of the same
+    rows), as bench.py times it: sampled requests against the oracle and the
+    unquantised bf16 oracle."""
+    print("[parity-full] split cache bs256 kv8192", flush=True)
+    B, L, P = 256, 8192, 8
+    case = synth.make_case(B, L, P, shuffle=True, seed=synth.BASE_SEED + 70, device=DEV)
+    k, ks = mla.quantize_mxfp4(case["kv"])
+    v, vs = mla.quantize_fp8(case["kv"])
+    qp, qe = mla.quantize_mxfp4(case["q"].reshape(B * 16, 576))
+    S = 2
+    out = mla.decode_mixed(qp.reshape(B, 16, 288), k, ks, v, vs, case["kv_indptr"], case["page_table"], P, S,
+                           q_scale=qe).cpu()
+    pt = case["page_table"].cpu().numpy()
+    vsc = orc.fp8_scale_from_amax(orc.amax_bf16(bits(case["kv"])))
+    assert float(vs.item()) == vsc
+    for b in (0, 77, 255):
+        gpos = b * L + np.arange(L)
+        rows = torch.from_numpy(pt[gpos // P].astype(np.int64) * P + gpos % P).to(DEV)
+        sub_kv = case["kv"][rows].cpu()
+        packed, e8 = orc.quant_mxfp4(bits(sub_kv))
+        codes, _ = orc.quant_fp8(bits(sub_kv), vsc)
+        assert np.array_equal(packed, u8(k[rows])) and np.array_equal(e8, u8(ks[rows]))
+        assert np.array_equal(codes, u8(v[rows]))
+        qpk, qe8 = orc.quant_mxfp4(bits(case["q"][b].cpu()))
+        sub = {"kv_indptr": torch.tensor([0, L], dtype=torch.int32), "page_table": torch.arange(L, dtype=torch.int32),
+               "page_indptr": None, "page_size": 1}
+        o = {"q": qpk.reshape(1, 16, 288), "q_dtype": "mxfp4", "q_e8m0": qe8, "kv": packed, "kv_e8m0": e8,
+             "v": codes, "v_scale": vsc}
+        heads = [0, 9, 15]
+        ref, _ = oracle_mixed(sub, o, orc, pairs=[(0, h) for h in heads])
+        sub["q"], sub["kv"] = case["q"][b:b + 1].cpu(), sub_kv
+        ref16 = bf16_reference(sub, orc, pairs=[(0, h) for h in heads])
+        for h in heads:
+            check_close(out[b, h], ref[0, h], what=f"mixed full b={b} h={h}", l2=1e-2)
+            check_close(out[b, h], ref16[0, h], atol=0.1, rtol=0.1, l2=None, what="mixed vs unquantised bf16")
+    assert torch.isfinite(out.float()).all()

@@ -218,3 +218,39 @@ def test_rows_workspace_bytes(lib):
         assert lib.mla_workspace_bytes_rows(b, 64, s) == 4 * lib.mla_workspace_bytes(b, s)
     assert lib.mla_workspace_bytes_rows(4, 8, 2) == 0
     assert lib.mla_workspace_bytes_rows(4, 2048, 2) == 0
+
+
+def vm(lib, q=A, qd=mla.BF16, qs=None, qr=16, k=A, ks=A2, vc=A, vs=A2, rows=100, ind=A, batch=4, pt=A,
+       pind=None, P=1, S=1, out=A, ws=None, wsb=0):
+    return lib.mla_validate_mixed(q, qd, qs, qr, k, ks, vc, vs, rows, ind, batch, pt, pind, P, S, out, ws, wsb)
+
+
+def test_validate_mixed(lib):
+    assert vm(lib) == 0
+    assert vm(lib, qd=mla.MXFP4, qs=A2) == 0
+    assert vm(lib, qd=mla.FP8, qs=A2) == -2          # fp8 Q is not a split-cache pair
+    assert vm(lib, qd=mla.MXFP4) == -1               # mxfp4 Q needs its scales
+    assert vm(lib, ks=None) == -1                    # key block scales
+    assert vm(lib, vc=None) == -1
+    assert vm(lib, vs=None) == -1
+    assert vm(lib, vc=A + 8) == -4
+    assert vm(lib, vs=A2 + 2) == -4
+    assert vm(lib, ks=A2 + 4) == -4
+    assert vm(lib, qr=24) == -3
+    assert vm(lib, qr=0) == -3
+    assert vm(lib, S=0) == -3
+    need = lib.mla_workspace_bytes_rows(4, 64, 8)
+    assert vm(lib, qr=64, S=8, ws=A2, wsb=need - 1) == -5
+    assert vm(lib, qr=64, S=8, ws=A2, wsb=need) == 0
+    assert vm(lib, batch=0, q=None, out=None, vc=None) == 0   # empty batch: nothing to do
+    # mla_decode itself does not take the split-cache code
+    assert v(lib, kd=mla.MIXED, ks=A2) == -2
+
+
+def test_split_heuristic_mixed(lib):
+    for batch in (1, 4, 32, 64, 256):
+        for L in (1, 1024, 8192):
+            s = mla.choose_num_splits(batch, L, mla.MIXED)
+            assert 1 <= s <= 256 and (s == 1 or (L + s - 1) // s >= 32)
+    assert mla.choose_num_splits(256, 8192, mla.MIXED) == 1
+    assert mla.choose_num_splits(4, 8192, mla.MIXED) >= 16
