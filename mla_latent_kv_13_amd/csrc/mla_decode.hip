@@ -111,9 +111,10 @@ template <int KF> struct Lay {
   static constexpr int kNbuf = Kv<KF>::kNbuf;
   static constexpr int kSlot = Kv<KF>::kUnits * 512;           // 32 tokens x row
   static constexpr int kScSlot = Kv<KF>::kNdmaSc ? 768 : 0;     // 3 x 64 dwords
-  static constexpr int kParSlot = Kv<KF>::kNdmaSc ? 32 : 0;     // row parity per token
+  static constexpr int kParSlot = Kv<KF>::kNdmaSc ? 16 : 0;     // row parity bit per token (one word, padded)
   static constexpr int kD = kNbuf > 1 ? kNbuf - 1 : 1;          // page-id prefetch distance
-  static constexpr int kNpid = kD + 1;
+  // page-id ring: a power of two >= kD + 1, so the ring index is a mask
+  static constexpr int kNpid = kD + 1 <= 2 ? 2 : 4;
   static constexpr int kPidSlot = 256;                          // 64 lanes x 4 B
   static constexpr int kScOff = kNbuf * kSlot;
   static constexpr int kParOff = kScOff + kNbuf * kScSlot;
@@ -126,6 +127,11 @@ template <int KF> struct Lay {
   static constexpr int kCombine = kWaves * 32768 + 2 * kWaves * kHeads * 4;  // 4 partial O^T + (m, l)
   static constexpr int kTotal = kWaves * kWaveBytes > kCombine ? kWaves * kWaveBytes : kCombine;
   static constexpr int kNdma = Kv<KF>::kNdmaX4 + Kv<KF>::kNdmaSc;  // VMEM instrs per sub-tile
+  // every region starts 16-byte aligned: the DMA writes and the row-pointer
+  // table need it
+  static_assert(kSlot % 16 == 0 && kScOff % 16 == 0 && kParOff % 16 == 0 && kPidOff % 16 == 0 &&
+                    kRowOff % 16 == 0 && kPtrOff % 16 == 0 && kWaveBytes % 16 == 0,
+                "per-wave LDS regions must stay 16-byte aligned");
 };
 
 // A sub-tile is stored as its row-major byte stream: token t's 16-byte unit k
@@ -204,8 +210,9 @@ __device__ __forceinline__ void pin8(T* v) {
 }
 
 
+// 2^(e-127), exact for every code including e = 0 (a denormal)
 __device__ __forceinline__ float e8m0_f32(uint32_t e) {
-  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+  return __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(e) - 127);
 }
 
 __device__ __forceinline__ uint32_t bits(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
@@ -511,7 +518,7 @@ void stage1_kernel(Stage1Args a) {
   auto slot_addr = [&](int x) { return wbase + static_cast<uint32_t>(x) * L::kSlot; };
   auto sc_addr = [&](int x) { return wbase + L::kScOff + static_cast<uint32_t>(x) * L::kScSlot; };
   auto par_addr = [&](int x) { return wbase + L::kParOff + static_cast<uint32_t>(x) * L::kParSlot; };
-  auto pid_addr = [&](int y) { return wbase + L::kPidOff + static_cast<uint32_t>(y % L::kNpid) * L::kPidSlot; };
+  auto pid_addr = [&](int y) { return wbase + L::kPidOff + static_cast<uint32_t>(y & (L::kNpid - 1)) * L::kPidSlot; };
 
 
   auto issue_pid = [&](int X) {
@@ -571,8 +578,10 @@ void stage1_kernel(Stage1Args a) {
         dma_x4_nt(reinterpret_cast<const char*>(rptr[i - I0]) + (dmao[i] & 0xffff), slot_addr(X % NBUF) + 1024u * i);
     }
   };
-  auto issue_tile = [&](int X, bool full) {
-    const int x = X % NBUF;
+  // tile X goes to slot x (= X mod NBUF, tracked by the caller: a modulo
+  // here would put a subtraction into every LDS address of the slot and keep
+  // the compiler from folding the constant offsets)
+  auto issue_tile = [&](int X, int x, bool full) {
     wait_lgkm0();  // every LDS read of the slot being refilled has completed
     const int ub = kSub * (w + kWaves * X);
     const int nv = min(kSub, n - ub);
@@ -581,16 +590,22 @@ void stage1_kernel(Stage1Args a) {
     // physical row (and its base address) of each of the 32 tokens; tokens
     // past the end repeat the last valid one, so a tail sub-tile stays finite
     // and in bounds
+    uint32_t row = 0;
     if (lane < kSub) {
       const int tok = ub + min(lane, nv - 1);
       const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
       const uint32_t pid = static_cast<uint32_t>(lds_ld<int>(static_cast<int>(pid_addr(X)) + 4 * lane));
-      const uint32_t row = pid * P + gpos % P;
+      row = pid * P + gpos % P;
       lds_st<uint32_t>(rt + 4 * lane, row);
       lds_st<uint64_t>(pt + 8 * lane, reinterpret_cast<uint64_t>(a.kv + static_cast<int64_t>(row) * ROW));
       if constexpr (KF == FMIX)
         lds_st<uint64_t>(pt + 8 * kSub + 8 * lane, reinterpret_cast<uint64_t>(a.kv2 + static_cast<int64_t>(row) * kDqk));
-      if constexpr (kMxK) lds_st<uint8_t>(static_cast<int>(par_addr(x)) + lane, static_cast<uint8_t>(row & 1));
+    }
+    // mxfp4 scale rows are 18 bytes, staged as aligned dwords: bit t of the
+    // slot's parity word says token t's row starts 2 bytes into its window
+    if constexpr (kMxK) {
+      const uint32_t pm = static_cast<uint32_t>(__ballot(lane < kSub && (row & 1u)));
+      if (lane == 0) lds_st<uint32_t>(static_cast<int>(par_addr(x)), pm);
     }
     // Row-pointer reads in batches of up to 18 (one LDS latency per batch),
     // each batch followed by its DMA instructions.
@@ -684,6 +699,9 @@ void stage1_kernel(Stage1Args a) {
   // pend: tile whose DMAs [KA, 18) are still to be issued (split mode), or -1
   auto compute = [&](int x, int ntok, int pend) {
     const int tb = static_cast<int>(slot_addr(x));
+    // mxfp4 scale-row parities of the slot's 32 tokens (one broadcast read)
+    uint32_t pmask = 0;
+    if constexpr (kMxK) pmask = lds_ld<uint32_t>(static_cast<int>(par_addr(x)));
 #pragma unroll
     for (int c = 0; c < 32; c += 8) pin_acc8(acc + c);
     // fp8 V^T fragments for P*V, one transposing read per 16-column tile:
@@ -789,9 +807,8 @@ void stage1_kernel(Stage1Args a) {
         }
       }
     } else {  // mxfp4 K: block scales read once per (token, block)
-      const int pr = static_cast<int>(par_addr(x));
-      const int sb0 = static_cast<int>(sc_addr(x)) + 20 * tq0 + 2 * lds_ld<uint8_t>(pr + tq0);
-      const int sb1 = static_cast<int>(sc_addr(x)) + 20 * tq1 + 2 * lds_ld<uint8_t>(pr + tq1);
+      const int sb0 = static_cast<int>(sc_addr(x)) + 20 * tq0 + 2 * ((pmask >> tq0) & 1u);
+      const int sb1 = static_cast<int>(sc_addr(x)) + 20 * tq1 + 2 * ((pmask >> tq1) & 1u);
       {
         i32x4_t u0[5], u1[5];
         uint32_t c0[5], c1[5];
@@ -931,19 +948,25 @@ void stage1_kernel(Stage1Args a) {
       // mxfp4: lane (column block i = lane&15) decodes unit i of its 8 tokens;
       // output tile c row r <-> latent column 32*(4g+r) + c.
       const int i = lane & 15;
-      const int sc0 = static_cast<int>(sc_addr(x));
-      const int pr0 = static_cast<int>(par_addr(x));
+      // lane bases of token 4g, made opaque so that every read below adds
+      // only an immediate offset (token 4g + kk is + 16 U kk bytes of codes
+      // and + 20 kk bytes of scales; tokens 16 + 4g + kk are 16 further)
+      int vbase = tb + 16 * (4 * g * U + i);
+      int sbase = static_cast<int>(sc_addr(x)) + 20 * 4 * g + i;
+      asm volatile("" : "+v"(vbase), "+v"(sbase));
+      const uint32_t pl = pmask >> (4 * g);  // parity of token 4g + k at bit k
       uint32_t vw[8][4];
       float vsc[8];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const int tv = kk < 4 ? 4 * g + kk : 16 + 4 * g + (kk - 4);
-        const i32x4_t u = lds_ld<i32x4_t>(tb + 16 * (tv * U + i));
+        const int dt = kk < 4 ? kk : 16 + (kk - 4);  // token offset from 4g
+        const i32x4_t u = lds_ld<i32x4_t>(vbase + 16 * U * dt);
         vw[kk][0] = u.x;
         vw[kk][1] = u.y;
         vw[kk][2] = u.z;
         vw[kk][3] = u.w;
-        vsc[kk] = e8m0_f32(lds_ld<uint8_t>(sc0 + 20 * tv + 2 * lds_ld<uint8_t>(pr0 + tv) + i));
+        const int sa = sbase + 2 * static_cast<int>(__builtin_amdgcn_ubfe(pl, dt, 1));
+        vsc[kk] = e8m0_f32(lds_ld<uint8_t>(sa + 20 * dt));
       }
       sched_fence();
 #pragma unroll
@@ -980,13 +1003,14 @@ void stage1_kernel(Stage1Args a) {
       issue_pid(X + D);
       // split mode: the second fill tile leaves its rest to compute(0)
       const bool full = !kSplitDma || X == 0;
-      issue_tile(X, full);
+      issue_tile(X, X, full);
       if (!full) pend = X;
     }
     if constexpr (kSplitQ) {
 #pragma unroll
       for (int c = 0; c < NQ; ++c) split_q_fp8(qraw + 4 * c, g, q8[c], ql[c], qhs[c], qls[c]);
     }
+    int xs = 0;  // slot of tile jx
     for (int jx = 0; jx < nloc; ++jx) {
       const int ahead = min(nloc - 1, jx + NBUF - 1) - jx;
       if constexpr (NBUF == 1) {
@@ -1002,15 +1026,16 @@ void stage1_kernel(Stage1Args a) {
         else wait_vm<0>();
       }
       const int ubase = kSub * (w + kWaves * jx);
-      compute(jx % NBUF, min(kSub, n - ubase), pend);
+      compute(xs, min(kSub, n - ubase), pend);
       pend = -1;
       const int X = jx + NBUF;
       if (X < nloc) {
         wait_vm<D * NDMA + D - 1>();
         issue_pid(X + D);
-        issue_tile(X, !kSplitDma);
+        issue_tile(X, xs, !kSplitDma);
         if (kSplitDma) pend = X;
       }
+      xs = xs + 1 == NBUF ? 0 : xs + 1;
     }
   }
 
