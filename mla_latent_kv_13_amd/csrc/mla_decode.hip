@@ -1133,20 +1133,28 @@ void stage1_kernel(Stage1Args a) {
 }
 
 // ------------------------------------------------------------------ stage 2
-// One workgroup per (request, group of 4 heads); a thread merges 8 columns of
-// one head over the S splits with base-2 log-sum-exp weights (empty splits,
-// LSE = -inf, are skipped; an all-empty request yields zeros).  One pass: the
-// LSEs and partial rows of eight splits are loaded together, the next eight
-// are in flight while they are combined, and the running maximum moves with a
-// rescale of the accumulator.
+// A thread merges kC columns of one head over the S splits with base-2
+// log-sum-exp weights (empty splits, LSE = -inf, are skipped; an all-empty
+// request yields zeros); a workgroup covers four heads x 512 / kParts columns
+// of one query group.  The LSEs and partial rows of kB splits are loaded
+// together; with kPre the next kB are in flight while a batch is combined,
+// and the running maximum moves with a rescale of the accumulator.  17 to 32
+// splits are taken in a single batch of loads (one memory round trip), with
+// four columns per thread so twice as many workgroups share the reads.
+template <int kB, int kC, bool kPre>
 __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
                                                      uint16_t* __restrict__ out, int S, const int32_t* __restrict__ req,
                                                      int G) {
-  const int v = blockIdx.x >> 2;  // query group (request b, group r)
+  static_assert(kC == 4 || kC == 8, "four or eight columns per thread");
+  constexpr int kParts = 8 / kC;  // column parts of a head row
+  constexpr int kV = kC / 4;      // f32x4 per split per thread
+  const int per_v = 4 * kParts;
+  const int v = blockIdx.x / per_v;  // query group (request b, group r)
+  const int hb = blockIdx.x - v * per_v;
   const int b = v / G;
   const int r = v - b * G;
-  const int hq = ((blockIdx.x & 3) << 2) + (threadIdx.x >> 6);
-  const int col = 8 * (threadIdx.x & 63);
+  const int hq = 4 * (hb / kParts) + (threadIdx.x >> 6);
+  const int col = (hb % kParts) * (kDv / kParts) + kC * (threadIdx.x & 63);
   // a request's partials: slots [base, base + S) (work list: from the plan;
   // a single-item request was written by stage 1); slot si of group r holds
   // rows ((base + si) * G + r) * 16 + [0, 16)
@@ -1160,26 +1168,48 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
   const float* lse = part_lse + (base * G + r) * kHeads + hq;
   const float* po = part_o + ((base * G + r) * kHeads + hq) * kDv + col;
   constexpr float kNegInf = -__builtin_huge_valf();
-  constexpr int kB = 8;
   float M = kNegInf, ws = 0.0f;
-  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  // batch loads: splits [s0, s0 + kB), past the end a repeat weighted 0 below
-  float l[kB], ln[kB];
-  f32x4_t x0[kB], x1[kB], y0[kB], y1[kB];
-  auto load = [&](int s0, float* lb, f32x4_t* b0, f32x4_t* b1) {
+  f32x4_t acc[kV];
 #pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      const int si = min(s0 + i, S - 1);
-      lb[i] = lse[si * stride];
-      b0[i] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv);
-      b1[i] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv + 4);
+  for (int k = 0; k < kV; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // batch loads: splits [s0, s0 + kB), past the end weighted 0
+  float l[kB], ln[kPre ? kB : 1];
+  f32x4_t x[kB][kV], y[kPre ? kB : 1][kV];
+  auto load = [&](int s0, float* lb, f32x4_t (*bx)[kV]) {
+    if constexpr (kB > 8) {
+      // a single wide batch: only the splits that exist are loaded
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        lb[i] = kNegInf;
+#pragma unroll
+        for (int k = 0; k < kV; ++k) bx[i][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (s0 + i < S) {
+          lb[i] = lse[(s0 + i) * stride];
+#pragma unroll
+          for (int k = 0; k < kV; ++k)
+            bx[i][k] = *reinterpret_cast<const f32x4_t*>(po + (s0 + i) * stride * kDv + 4 * k);
+        }
+      }
+    } else {
+      // all kB loads unconditional (past the end: the last split again, a
+      // cache hit), so they are in flight together
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        const int si = min(s0 + i, S - 1);
+        lb[i] = lse[si * stride];
+#pragma unroll
+        for (int k = 0; k < kV; ++k) bx[i][k] = *reinterpret_cast<const f32x4_t*>(po + si * stride * kDv + 4 * k);
+      }
     }
   };
-  load(0, l, x0, x1);
+  load(0, l, x);
   for (int s0 = 0; s0 < S; s0 += kB) {
-    // the next batch is in flight while this one is combined
     const bool more = s0 + kB < S;
-    if (more) load(s0 + kB, ln, y0, y1);
+    if constexpr (kPre) {
+      if (more) load(s0 + kB, ln, y);
+    } else {
+      if (s0 > 0) load(s0, l, x);
+    }
 #pragma unroll
     for (int i = 0; i < kB; ++i)
       if (s0 + i >= S) l[i] = kNegInf;
@@ -1188,37 +1218,44 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
     for (int i = 1; i < kB; ++i) mb = fmax3(mb, l[i]);
     if (mb != kNegInf) {  // else every split of this batch is empty
       const float Mn = fmax3(M, mb);
-      const float r = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-      a0 *= r;
-      a1 *= r;
-      ws *= r;
+      const float rs = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+#pragma unroll
+      for (int k = 0; k < kV; ++k) acc[k] *= rs;
+      ws *= rs;
 #pragma unroll
       for (int i = 0; i < kB; ++i) {
         const float wgt = l[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(l[i] - Mn);
-        a0 += x0[i] * wgt;
-        a1 += x1[i] * wgt;
+#pragma unroll
+        for (int k = 0; k < kV; ++k) acc[k] += x[i][k] * wgt;
         ws += wgt;
       }
       M = Mn;
     }
-    if (more) {
+    if constexpr (kPre) {
+      if (more) {
 #pragma unroll
-      for (int i = 0; i < kB; ++i) {
-        l[i] = ln[i];
-        x0[i] = y0[i];
-        x1[i] = y1[i];
+        for (int i = 0; i < kB; ++i) {
+          l[i] = ln[i];
+#pragma unroll
+          for (int k = 0; k < kV; ++k) x[i][k] = y[i][k];
+        }
       }
     }
   }
   const float inv = ws > 0.0f ? 1.0f / ws : 0.0f;
-  a0 *= inv;
-  a1 *= inv;
-  u32x4_t o;
-  o.x = bits(bf16x2_t{static_cast<__bf16>(a0.x), static_cast<__bf16>(a0.y)});
-  o.y = bits(bf16x2_t{static_cast<__bf16>(a0.z), static_cast<__bf16>(a0.w)});
-  o.z = bits(bf16x2_t{static_cast<__bf16>(a1.x), static_cast<__bf16>(a1.y)});
-  o.w = bits(bf16x2_t{static_cast<__bf16>(a1.z), static_cast<__bf16>(a1.w)});
-  *reinterpret_cast<u32x4_t*>(out + (static_cast<size_t>(v) * kHeads + hq) * kDv + col) = o;
+  uint32_t o[2 * kV];
+#pragma unroll
+  for (int k = 0; k < kV; ++k) {
+    const f32x4_t a = acc[k] * inv;
+    o[2 * k] = bits(bf16x2_t{static_cast<__bf16>(a.x), static_cast<__bf16>(a.y)});
+    o[2 * k + 1] = bits(bf16x2_t{static_cast<__bf16>(a.z), static_cast<__bf16>(a.w)});
+  }
+  uint16_t* op = out + (static_cast<size_t>(v) * kHeads + hq) * kDv + col;
+  if constexpr (kV == 2) {
+    *reinterpret_cast<u32x4_t*>(op) = u32x4_t{o[0], o[1], o[2], o[3]};
+  } else {
+    *reinterpret_cast<i32x2_t*>(op) = i32x2_t{static_cast<int>(o[0]), static_cast<int>(o[1])};
+  }
 }
 
 // -------------------------------------------------------------- quantisers
@@ -1434,8 +1471,19 @@ int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q
   const int64_t grid = G == 1 ? units : (units + 7) / 8 * 8 * G;
   if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(grid), st) != hipSuccess) return MLA_ERR_LAUNCH;
   if (need) {
-    hipLaunchKernelGGL(stage2_kernel, dim3(static_cast<unsigned>(batch) * G * 4), dim3(256), 0, st, a.part_o,
-                       a.part_lse, static_cast<uint16_t*>(out), items ? 1 : num_splits, items ? req : nullptr, G);
+    // 17 to 32 splits: one batch of loads, four columns per thread; other
+    // counts (and work lists, whose per-request counts live on the device):
+    // batches of eight with the next batch in flight
+    const int S2 = items ? 1 : num_splits;
+    const int32_t* rq = items ? req : nullptr;
+    uint16_t* o16 = static_cast<uint16_t*>(out);
+    const unsigned vg = static_cast<unsigned>(batch) * G;
+    if (!items && num_splits > 16 && num_splits <= 32)
+      hipLaunchKernelGGL((stage2_kernel<32, 4, false>), dim3(vg * 8), dim3(256), 0, st, a.part_o, a.part_lse, o16, S2,
+                         rq, G);
+    else
+      hipLaunchKernelGGL((stage2_kernel<8, 8, true>), dim3(vg * 4), dim3(256), 0, st, a.part_o, a.part_lse, o16, S2,
+                         rq, G);
     if (hipGetLastError() != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;

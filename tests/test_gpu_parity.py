@@ -186,7 +186,7 @@ def test_split_count_invariance(orc, kf):
     case = synth.make_case(3, [700, 129, 1], 8, shuffle=True, seed=500)
     g, o = prepare(case, "bf16", kf, orc)
     ref, _ = oracle_decode(case, o, orc)
-    for S in (1, 2, 3, 8, 32, 256):
+    for S in (1, 2, 3, 8, 9, 16, 17, 32, 33, 256):  # every stage-2 batching mode and its edges
         check_close(gpu_decode(case, g, S), ref, what=f"{kf} S={S}")
 
 
