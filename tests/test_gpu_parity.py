@@ -639,3 +639,64 @@ def test_full_size_mixed(orc):
             check_close(out[b, h], ref[0, h], what=f"mixed full b={b} h={h}", l2=1e-2)
             check_close(out[b, h], ref16[0, h], atol=0.1, rtol=0.1, l2=None, what="mixed vs unquantised bf16")
     assert torch.isfinite(out.float()).all()
+
+
+# ---------------------------------------------------------- maximum sizes
+@pytest.mark.parametrize("kf", ["fp8", "mxfp4"])
+def test_cache_beyond_4gb(orc, kf):
+    """A cache larger than 4 GiB whose used pages sit at its top, so every row
+    offset the kernel forms exceeds 32 bits."""
+    P = 8
+    case = synth.make_case(2, [1000, 777], P, shuffle=True, seed=990, extra_pages=1)
+    g, o = prepare(case, "bf16", kf, orc)
+    row_bytes = 576 if kf == "fp8" else 288
+    rows_big = ((5 << 30) // row_bytes + P - 1) // P * P  # 5 GiB of rows, whole pages
+    n_small = case["kv"].shape[0]
+    off = rows_big - n_small  # a multiple of P: the small cache's pages move up by off / P
+    print(f"[parity-max] {kf} cache of {rows_big} rows ({rows_big * row_bytes / 2**30:.2f} GiB), offset {off}",
+          flush=True)
+    if kf == "fp8":
+        big = torch.empty((rows_big, 576), dtype=torch.float8_e4m3fn, device=DEV)
+        big.view(torch.uint8)[off:] = g["kv"].view(torch.uint8)
+        big_scale = g["kv_scale"]
+    else:
+        big = torch.empty((rows_big, 288), dtype=torch.uint8, device=DEV)
+        big[off:] = g["kv"]
+        big_scale = mla.mxfp4_scale_buffer(rows_big, DEV)
+        big_scale[off:] = g["kv_scale"]
+    pt = (case["page_table"].to(DEV) + off // P).contiguous()
+    ref, _ = oracle_decode(case, o, orc)
+    for S in (1, 3):
+        out = mla.decode(g["q"], big, g["kv_indptr"], pt, P, S, kv_scale=big_scale)
+        torch.cuda.synchronize()
+        check_close(out, ref, what=f"{kf} cache beyond 4 GiB, S={S}")
+    del big, big_scale
+    torch.cuda.empty_cache()
+
+
+def test_max_q_rows(orc):
+    """q_rows at its maximum (1024 rows = 64 query groups per request)."""
+    lengths = [300, 33]
+    case = synth.make_case(2, lengths, 8, shuffle=True, seed=991)
+    case["q"] = synth.normal_bf16((2, 1024, 576), seed=992)
+    g, o = prepare(case, "bf16", "fp8", orc)
+    ref, _ = oracle_decode(case, o, orc)
+    for S in (1, 2):
+        out = gpu_decode(case, g, S)
+        assert out.shape == (2, 1024, 512)
+        check_close(out, ref, what=f"1024 rows S={S}")
+    with pytest.raises(mla.StatusError):  # one group more than the maximum
+        q_over = synth.normal_bf16((2, 1040, 576), seed=993, device=DEV)
+        mla.decode(q_over, g["kv"], g["kv_indptr"], g["page_table"], 8, 1, kv_scale=g["kv_scale"])
+
+
+@pytest.mark.parametrize("kf", ["bf16", "mxfp4"])
+def test_large_page_size(orc, kf):
+    """Pages of 256 rows, per-request tables, ragged lengths that end inside a
+    page, more splits than a page holds sub-tiles."""
+    lengths = [700, 1, 513, 256]
+    case = synth.make_case(len(lengths), lengths, 256, shuffle=True, seed=994, per_request_pages=True, extra_pages=2)
+    g, o = prepare(case, "bf16", kf, orc)
+    ref, _ = oracle_decode(case, o, orc)
+    for S in (1, 5):
+        check_close(gpu_decode(case, g, S), ref, what=f"page 256 {kf} S={S}")
