@@ -47,8 +47,10 @@ namespace {
 constexpr int kHeads = 16;
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Waves per stage-1 workgroup: four, or two when the grid has more
+// workgroups than the chip has CUs -- two such workgroups then share a CU
+// (each fits half its LDS) and the grid runs in one round instead of two.
+constexpr int kMaxWaves = 4;
 constexpr int kSub = 32;  // tokens per wave sub-tile
 
 constexpr int FBF16 = MLA_DTYPE_BF16;
@@ -107,7 +109,7 @@ template <> struct Kv<FMIX> {
   static constexpr int kNbuf = 1;
 };
 
-template <int KF> struct Lay {
+template <int KF, int kWaves = kMaxWaves> struct Lay {
   static constexpr int kNbuf = Kv<KF>::kNbuf;
   static constexpr int kSlot = Kv<KF>::kUnits * 512;           // 32 tokens x row
   static constexpr int kScSlot = Kv<KF>::kNdmaSc ? 768 : 0;     // 3 x 64 dwords
@@ -124,7 +126,7 @@ template <int KF> struct Lay {
   // split cache: the V rows' base addresses follow the K rows'
   static constexpr int kPtrBytes = (KF == FMIX ? 2 : 1) * 8 * kSub;
   static constexpr int kWaveBytes = kPtrOff + kPtrBytes;
-  static constexpr int kCombine = kWaves * 32768 + 2 * kWaves * kHeads * 4;  // 4 partial O^T + (m, l)
+  static constexpr int kCombine = kWaves * 32768 + 2 * kWaves * kHeads * 4;  // per-wave O^T + (m, l)
   static constexpr int kTotal = kWaves * kWaveBytes > kCombine ? kWaves * kWaveBytes : kCombine;
   static constexpr int kNdma = Kv<KF>::kNdmaX4 + Kv<KF>::kNdmaSc;  // VMEM instrs per sub-tile
   // every region starts 16-byte aligned: the DMA writes and the row-pointer
@@ -384,10 +386,13 @@ __device__ __forceinline__ int qdim_bf16(int m, int g) {
 }
 
 // ------------------------------------------------------------------ stage 1
-template <int QF, int KF>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int QF, int KF, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stage1_kernel(Stage1Args a) {
-  using L = Lay<KF>;
+  static_assert(kWaves == 2 || kWaves == 4, "two or four waves");
+  using L = Lay<KF, kWaves>;
+  // two-wave workgroups must fit two to a CU
+  static_assert(kWaves == 4 || 2 * L::kTotal <= 160 * 1024, "LDS of two workgroups exceeds a CU");
   constexpr int NBUF = L::kNbuf;
   constexpr int D = L::kD;
   constexpr int NDMA = L::kNdma;
@@ -1039,11 +1044,13 @@ void stage1_kernel(Stage1Args a) {
     }
   }
 
-  // ---- merge the four waves (log2-domain weights), then write.  Every wave
-  // parks its O^T fragments and (m, l) in LDS (the staging rings are idle
-  // now), then wave v merges fragments 8v..8v+7 -- a quarter of the output
-  // columns -- over the four waves and stores them, so one barrier separates
-  // the two halves and the output stores are spread over the waves.
+  // ---- merge the waves (log2-domain weights), then write.  Every wave parks
+  // its O^T fragments and (m, l) in LDS (the staging rings are idle now),
+  // then wave v merges fragments F v .. F v + F - 1 (F = 32 / waves, its
+  // share of the output columns) over all waves and stores them, so one
+  // barrier separates the two halves and the output stores are spread over
+  // the waves.
+  constexpr int F = 32 / kWaves;
   l_run = group_sum(l_run);
   __syncthreads();
   const int ob0 = static_cast<int>(smem0);
@@ -1061,11 +1068,11 @@ void stage1_kernel(Stage1Args a) {
     mw[v] = lds_ld<float>(mlb + (v * kHeads + hq) * 4);
     lw[v] = lds_ld<float>(mlb + (kWaves * kHeads + v * kHeads + hq) * 4);
   }
-  f32x4_t part[kWaves][8];
+  f32x4_t part[kWaves][F];
 #pragma unroll
   for (int v = 0; v < kWaves; ++v)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) part[v][i] = lds_ld<f32x4_t>(ob0 + v * 32768 + ((8 * w + i) * 64 + lane) * 16);
+    for (int i = 0; i < F; ++i) part[v][i] = lds_ld<f32x4_t>(ob0 + v * 32768 + ((F * w + i) * 64 + lane) * 16);
   sched_fence();
   float M = mw[0];
 #pragma unroll
@@ -1077,9 +1084,9 @@ void stage1_kernel(Stage1Args a) {
     fv[v] = mw[v] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mw[v] - M);
     lsum += lw[v] * fv[v];
   }
-  f32x4_t o[8];
+  f32x4_t o[F];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < F; ++i) {
     o[i] = part[0][i] * fv[0];
 #pragma unroll
     for (int v = 1; v < kWaves; ++v) o[i] += part[v][i] * fv[v];
@@ -1090,7 +1097,7 @@ void stage1_kernel(Stage1Args a) {
   const float lse = nonempty ? M + __builtin_amdgcn_logf(lsum) : -__builtin_huge_valf();
   const size_t orow = static_cast<size_t>(v) * kHeads + hq;
   const bool direct = a.items ? slot < 0 : S == 1;
-  // fragment c = 8w + i; non-mxfp4 row r of fragment c is output column
+  // fragment c = F w + i; non-mxfp4 row r of fragment c is output column
   // 16c + 4g + r, mxfp4 row r is column 32(4g + r) + c
   if (direct) {
     uint16_t* op = a.out + orow * kDv;
@@ -1098,18 +1105,18 @@ void stage1_kernel(Stage1Args a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int h4 = 0; h4 < 2; ++h4) {
+        for (int h4 = 0; h4 < F / 4; ++h4) {
           const bf16x2_t p0 = {static_cast<__bf16>(o[4 * h4 + 0][r] * mul), static_cast<__bf16>(o[4 * h4 + 1][r] * mul)};
           const bf16x2_t p1 = {static_cast<__bf16>(o[4 * h4 + 2][r] * mul), static_cast<__bf16>(o[4 * h4 + 3][r] * mul)};
-          *reinterpret_cast<i32x2_t*>(op + 32 * (4 * g + r) + 8 * w + 4 * h4) =
+          *reinterpret_cast<i32x2_t*>(op + 32 * (4 * g + r) + F * w + 4 * h4) =
               i32x2_t{static_cast<int>(bits(p0)), static_cast<int>(bits(p1))};
         }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < F; ++i) {
         const bf16x2_t p0 = {static_cast<__bf16>(o[i][0] * mul), static_cast<__bf16>(o[i][1] * mul)};
         const bf16x2_t p1 = {static_cast<__bf16>(o[i][2] * mul), static_cast<__bf16>(o[i][3] * mul)};
-        *reinterpret_cast<i32x2_t*>(op + 16 * (8 * w + i) + 4 * g) =
+        *reinterpret_cast<i32x2_t*>(op + 16 * (F * w + i) + 4 * g) =
             i32x2_t{static_cast<int>(bits(p0)), static_cast<int>(bits(p1))};
       }
     }
@@ -1121,12 +1128,12 @@ void stage1_kernel(Stage1Args a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int h4 = 0; h4 < 2; ++h4)
-          *reinterpret_cast<f32x4_t*>(po + 32 * (4 * g + r) + 8 * w + 4 * h4) =
+        for (int h4 = 0; h4 < F / 4; ++h4)
+          *reinterpret_cast<f32x4_t*>(po + 32 * (4 * g + r) + F * w + 4 * h4) =
               f32x4_t{o[4 * h4][r], o[4 * h4 + 1][r], o[4 * h4 + 2][r], o[4 * h4 + 3][r]} * mul;
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4_t*>(po + 16 * (8 * w + i) + 4 * g) = o[i] * mul;
+      for (int i = 0; i < F; ++i) *reinterpret_cast<f32x4_t*>(po + 16 * (F * w + i) + 4 * g) = o[i] * mul;
     }
     if (w == 0 && g == 0) a.part_lse[prow] = lse;
   }
@@ -1369,18 +1376,36 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
 
 // ------------------------------------------------------------------ launch
 template <int QF, int KF>
-hipError_t launch_stage1(const Stage1Args& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((stage1_kernel<QF, KF>), dim3(grid), dim3(kThreads), 0, st, a);
+hipError_t launch_stage1(const Stage1Args& a, unsigned grid, bool two_waves, hipStream_t st) {
+  if (two_waves)
+    hipLaunchKernelGGL((stage1_kernel<QF, KF, 2>), dim3(grid), dim3(128), 0, st, a);
+  else
+    hipLaunchKernelGGL((stage1_kernel<QF, KF, 4>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_stage1_any(const Stage1Args& a, int32_t q_dtype, int32_t kv_dtype, unsigned grid, hipStream_t st) {
-  if (kv_dtype == MLA_DTYPE_BF16) return launch_stage1<FBF16, FBF16>(a, grid, st);
+hipError_t launch_stage1_any(const Stage1Args& a, int32_t q_dtype, int32_t kv_dtype, unsigned grid, bool two_waves,
+                             hipStream_t st) {
+  const bool qb = q_dtype == MLA_DTYPE_BF16;
+  if (kv_dtype == MLA_DTYPE_BF16) return launch_stage1<FBF16, FBF16>(a, grid, two_waves, st);
   if (kv_dtype == MLA_DTYPE_FP8_E4M3FN)
-    return q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FFP8>(a, grid, st) : launch_stage1<FFP8, FFP8>(a, grid, st);
+    return qb ? launch_stage1<FBF16, FFP8>(a, grid, two_waves, st) : launch_stage1<FFP8, FFP8>(a, grid, two_waves, st);
   if (kv_dtype == MLA_KV_MXFP4_K_FP8_V)
-    return q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FMIX>(a, grid, st) : launch_stage1<FMX, FMIX>(a, grid, st);
-  return q_dtype == MLA_DTYPE_BF16 ? launch_stage1<FBF16, FMX>(a, grid, st) : launch_stage1<FMX, FMX>(a, grid, st);
+    return qb ? launch_stage1<FBF16, FMIX>(a, grid, two_waves, st) : launch_stage1<FMX, FMIX>(a, grid, two_waves, st);
+  return qb ? launch_stage1<FBF16, FMX>(a, grid, two_waves, st) : launch_stage1<FMX, FMX>(a, grid, two_waves, st);
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 int grid_for(int64_t n, int per) {
@@ -1469,7 +1494,10 @@ int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q
   a.num_splits = items ? 1 : num_splits;
   a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);  // log2(e) / sqrt(576)
   const int64_t grid = G == 1 ? units : (units + 7) / 8 * 8 * G;
-  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(grid), st) != hipSuccess) return MLA_ERR_LAUNCH;
+  // more workgroups than CUs: two-wave workgroups, two per CU, one round
+  const bool two_waves = grid > device_cus();
+  if (launch_stage1_any(a, q_dtype, kv_dtype, static_cast<unsigned>(grid), two_waves, st) != hipSuccess)
+    return MLA_ERR_LAUNCH;
   if (need) {
     // 17 to 32 splits: one batch of loads, four columns per thread; other
     // counts (and work lists, whose per-request counts live on the device):

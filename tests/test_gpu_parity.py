@@ -700,3 +700,33 @@ def test_large_page_size(orc, kf):
     ref, _ = oracle_decode(case, o, orc)
     for S in (1, 5):
         check_close(gpu_decode(case, g, S), ref, what=f"page 256 {kf} S={S}")
+
+
+# ------------------------------------------- more workgroups than compute units
+@pytest.mark.parametrize("qf,kf", PAIRS)
+def test_two_wave_workgroups(orc, qf, kf):
+    """A grid with more workgroups than the device has CUs runs two-wave
+    workgroups, two to a CU: short ragged requests (some empty, some of one
+    token) in batches of 300, with and without splits."""
+    B = 300
+    g_ = torch.Generator().manual_seed(995)
+    lengths = [int(x) for x in torch.randint(0, 160, (B,), generator=g_)]
+    lengths[0], lengths[1], lengths[-1] = 0, 1, 159
+    case = synth.make_case(B, lengths, 8, shuffle=True, seed=996)
+    g, o = prepare(case, qf, kf, orc)
+    ref, _ = oracle_decode(case, o, orc)
+    for S in (1, 3):
+        out = gpu_decode(case, g, S)
+        check_close(out, ref, what=f"{B} requests {qf}/{kf} S={S}")
+        assert not out[0].any()
+
+
+def test_two_wave_workgroups_split_cache(orc):
+    B = 280
+    g_ = torch.Generator().manual_seed(997)
+    lengths = [int(x) for x in torch.randint(1, 200, (B,), generator=g_)]
+    case = synth.make_case(B, lengths, 8, shuffle=True, seed=998)
+    g, o, _ = prepare_mixed(case, "mxfp4", orc, v_seed=999)
+    ref, _ = oracle_mixed(case, o, orc)
+    for S in (1, 2):
+        check_close(gpu_decode_mixed(case, g, S), ref, what=f"{B} requests split cache S={S}")
