@@ -8,7 +8,8 @@
 // 512 latent dims; the logit scale is 1/sqrt(576).  Stage 1 handles one
 // (request, split) per workgroup; stage 2 merges the splits.
 //
-// Stage-1 design (one workgroup = 4 independent waves):
+// Stage-1 design (one workgroup = 4 independent waves, or 2 when the grid has
+// more workgroups than the device has CUs, so that two workgroups share a CU):
 //   * A split's tokens are cut into 32-token sub-tiles dealt round-robin to the
 //     waves.  Each wave streams its sub-tiles HBM -> LDS with direct-to-LDS
 //     16-byte loads (global_load_lds_dwordx4) into a private ring of NBUF
@@ -19,7 +20,8 @@
 //     Q held in registers as the B operand.  bf16 x bf16 and bf16 x fp8 (fp8
 //     widened exactly to bf16) use v_mfma_f32_16x16x32_bf16; fp8 x fp8 and
 //     mxfp4 x mxfp4 use v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales for
-//     fp8, the e8m0 block scales for mxfp4).
+//     fp8, the e8m0 block scales for mxfp4); bf16 Q over mxfp4 K runs as an
+//     exact pair of fp8 operands on the same instruction.
 //   * Online softmax in the log2 domain.  The QK accumulator layout puts one
 //     head per lane, so the running max / sum are per-lane scalars and the
 //     P tile is already the B operand of P*V (no LDS round trip).
@@ -27,7 +29,7 @@
 //     SAME staged tile (no second HBM read): transposing LDS reads
 //     (ds_read_b64_tr_b16 / _b8) for bf16 / fp8, per-token e2m1->bf16
 //     conversion plus register shuffles for mxfp4.
-//   * The four waves merge their (max, sum, O) through LDS at the end; S == 1
+//   * The waves merge their (max, sum, O) through LDS at the end; S == 1
 //     writes bf16 out directly, otherwise fp32 partial O / base-2 LSE.
 //   * Split cache (page 695854's mxfp4 q=1 routes): K from the mxfp4 cache and
 //     V from the first 512 dims of an fp8 cache on the same rows.  Both rows
@@ -565,7 +567,7 @@ void stage1_kernel(Stage1Args a) {
   // With two slots per wave (fp8), a tile's DMAs are issued in three parts:
   // the first KA right after the slot is freed, the rest interleaved with the
   // next sub-tile's compute.  The address unit accepts a 1 KB direct-to-LDS
-  // load about every 16 clocks per CU, so a burst of 18 per wave (x4 waves)
+  // load about every 16 clocks per CU, so a burst of 18 per wave (x4 waves per CU)
   // would hold the wave at issue for most of a microsecond.
   constexpr bool kSplitDma = NBUF == 2;
   constexpr int KA = kSplitDma ? 6 : Kv<KF>::kNdmaX4;
