@@ -116,12 +116,19 @@ def time_calls(call, steps, warmup, warmup_s, per_graph=None):
     The calls are captured once into a graph of `per_graph` consecutive calls
     (call(i) for i in [0, per_graph)), so the GPU sees back-to-back kernels with
     no host launch overhead -- the way a serving loop issues decode.  After a
-    warm-up of at least `warmup` calls and `warmup_s` seconds, five groups of
-    whole graph replays are timed with HIP events on the launch stream.
+    warm-up of at least `warmup` calls and `warmup_s` seconds, groups of whole
+    graph replays are timed with HIP events on the launch stream: without
+    `per_graph`, exactly `steps` calls in up to five equal groups; with it
+    (rotated replicas), five groups of whole graphs covering at least `steps`.
     Returns (median, min, max) ms per call over the groups, the host wall time
     per call and the number of timed calls."""
-    ngroups = 5
-    per_graph = per_graph or max(1, steps // ngroups)
+    if per_graph is None:
+        # exactly `steps` timed calls: up to five equal groups of one graph each
+        steps = max(1, steps)
+        ngroups = next(g for g in (5, 4, 3, 2, 1) if steps % g == 0)
+        per_graph = steps // ngroups
+    else:
+        ngroups = 5
     reps_per_group = max(1, math.ceil(steps / (ngroups * per_graph)))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
