@@ -730,3 +730,18 @@ def test_two_wave_workgroups_split_cache(orc):
     ref, _ = oracle_mixed(case, o, orc)
     for S in (1, 2):
         check_close(gpu_decode_mixed(case, g, S), ref, what=f"{B} requests split cache S={S}")
+
+
+@pytest.mark.parametrize("S", [1, 16])
+def test_long_request(orc, S):
+    """One request of 131072 tokens (4096 sub-tiles, 1024 per wave at S = 1)
+    next to a short one, fp8 cache, page 8 shuffled; three heads of each
+    request against the oracle."""
+    lengths = [131072, 77]
+    case = synth.make_case(2, lengths, 8, shuffle=True, seed=1001)
+    g, o = prepare(case, "bf16", "fp8", orc)
+    out = gpu_decode(case, g, S).cpu()
+    pairs = [(0, 0), (0, 7), (0, 15), (1, 3)]
+    ref, _ = oracle_decode(case, o, orc, pairs=pairs)
+    for b, h in pairs:
+        check_close(out[b, h], ref[b, h], what=f"long request S={S} b={b} h={h}", l2=1e-2)
