@@ -285,7 +285,7 @@ int mla_quantize_mxfp4(const void* src_bf16, int64_t rows, int64_t cols, uint8_t
 /*
  * mla_stream_read - measurement helper, not part of the decode path.  Reads
  * `bytes` bytes (a multiple of 16) of the device buffer `src` (16-byte
- * aligned) once with 16-byte non-temporal loads spread over up to 16384
+ * aligned) once with 16-byte non-temporal loads spread over up to 131072
  * workgroups, folding them into one word that is written to `sink` (device,
  * 4 bytes) only if it equals a fixed improbable value.  Enqueued on `stream`;
  * its duration is the streaming-read ceiling of the device for a buffer of

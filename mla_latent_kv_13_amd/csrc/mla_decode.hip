@@ -1607,9 +1607,10 @@ int mla_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const int64_t n16 = bytes / 16;
-  // 64 workgroups per CU of 256-thread blocks: enough loads in flight to
-  // saturate HBM on every XCD.
-  const int64_t grid = std::min<int64_t>(16384, (n16 + 1023) / 1024);
+  // Many small chunks (at least 8 KB each, up to 131072 workgroups) keep the
+  // most DRAM channels busy at once: on MI355X the rate still rose from
+  // 16384 to 131072 workgroups over a 1.2 GB buffer (6.69 -> 7.06 TB/s).
+  const int64_t grid = std::min<int64_t>(131072, (n16 + 511) / 512);
   const int64_t per_block = (n16 + grid - 1) / grid;
   hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
                      static_cast<const u32x4_t*>(src), n16, per_block, sink);
