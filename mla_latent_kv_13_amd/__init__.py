@@ -12,6 +12,8 @@ Tensor conventions:
   fp8 e4m3fn data    torch.float8_e4m3fn (one fp32 per-tensor scale, a 1-element
                      float32 tensor on the device)
   mxfp4 data         torch.uint8 packed [..., 288] + torch.uint8 e8m0 scales [..., 18]
+  split cache        an mxfp4 key cache plus a float8_e4m3fn value cache on the same
+                     rows (decode_mixed)
 """
 from __future__ import annotations
 

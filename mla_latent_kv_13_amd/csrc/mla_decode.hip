@@ -538,8 +538,9 @@ void stage1_kernel(Stage1Args a) {
   // Per DMA instruction i, this lane fills LDS chunk 64i + lane = token t,
   // stored unit k (stream unit k ^ tswz(t)), packed as (8t << 16) | 16*(stream
   // unit): the row-pointer table offset and the byte offset inside the row.
-  // Formats with up to 18 instructions per sub-tile keep these in registers;
-  // bf16 (36) recomputes them from an opaque lane index instead.
+  // Every cache format keeps these in registers (bf16 36, split cache 25,
+  // fp8 18, mxfp4 9 per lane); the path that recomputes them from an opaque
+  // lane index serves any layout with more instructions per sub-tile.
   constexpr bool kPre = Kv<KF>::kNdmaX4 <= 36;
   auto dma_pack = [](int i, int ln) {
     if constexpr (KF == FMIX) {
