@@ -386,11 +386,11 @@ def test_invalid_arguments_raise():
 
 
 # ------------------------------------------------------- full-size workloads
-def sampled_check(w, orc, n_req=6, seed_offset=0):
-    print(f"[parity-full] {w.name}", flush=True)
+def sampled_check(w, orc, n_req=6, seed_offset=0, splits=None):
+    print(f"[parity-full] {w.name} splits={splits}", flush=True)
     case = synth.workload_case(w, device=DEV, seed_offset=seed_offset)
     B, P = w.batch, w.page_size
-    S = w.num_splits or mla.choose_num_splits(B, w.kv_len, {"bf16": 0, "fp8": 1, "mxfp4": 2}[w.kv_fmt])
+    S = splits or w.num_splits or mla.choose_num_splits(B, w.kv_len, {"bf16": 0, "fp8": 1, "mxfp4": 2}[w.kv_fmt])
     g = {"page_table": case["page_table"], "kv_indptr": case["kv_indptr"], "page_indptr": None}
     if w.kv_fmt == "fp8":
         g["kv"], g["kv_scale"] = mla.quantize_fp8(case["kv"])
@@ -454,6 +454,18 @@ def sampled_check(w, orc, n_req=6, seed_offset=0):
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_full_size_workload(orc, name):
     sampled_check(synth.WORKLOADS[name], orc)
+
+
+@pytest.mark.parametrize("name", [n for n, w in synth.WORKLOADS.items() if w.num_splits])
+def test_full_size_workload_heuristic_splits(orc, name):
+    """The same shapes at the library heuristic's split count, which bench.py
+    also times (it differs from the stated count for bs64 and the mxfp4
+    shapes: one round of four-wave workgroups instead of two-wave ones)."""
+    w = synth.WORKLOADS[name]
+    S = mla.choose_num_splits(w.batch, w.kv_len, {"bf16": 0, "fp8": 1, "mxfp4": 2}[w.kv_fmt])
+    if S == w.num_splits:
+        pytest.skip("the heuristic picks the stated split count")
+    sampled_check(w, orc, n_req=3, splits=S)
 
 
 def _sampled_fp8_rows(orc, case, g, out, reqs, rows_of_q, what):
