@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 #include <utility>
@@ -1398,17 +1399,18 @@ hipError_t launch_stage1_any(const Stage1Args& a, int32_t q_dtype, int32_t kv_dt
   return qb ? launch_stage1<FBF16, FMX>(a, grid, two_waves, st) : launch_stage1<FMX, FMX>(a, grid, two_waves, st);
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; concurrent
+// callers may both query, and store the same value).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 int grid_for(int64_t n, int per) {
@@ -1466,7 +1468,9 @@ int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q
   if (items && (!req)) return MLA_ERR_NULL;
   if (items && (num_items < batch || num_slots < 0)) return MLA_ERR_ARG;
   const int64_t units = items ? static_cast<int64_t>(num_items) : static_cast<int64_t>(batch) * num_splits;
-  if ((units + 7) * G > 0x7fffffffLL || static_cast<int64_t>(batch) * G * 4 > 0x7fffffffLL) return MLA_ERR_ARG;
+  // grid sizes must fit an unsigned 32-bit launch: stage 1 pads the units to
+  // a multiple of 8 per query group, stage 2 takes up to 8 workgroups per group
+  if ((units + 7) * G > 0x7fffffffLL || static_cast<int64_t>(batch) * G * 8 > 0x7fffffffLL) return MLA_ERR_ARG;
   const int64_t nslots = items ? num_slots : (num_splits > 1 ? static_cast<int64_t>(batch) * num_splits : 0);
   const size_t parts = static_cast<size_t>(nslots) * G * kHeads;
   const size_t need = parts * kDv * sizeof(float) + parts * sizeof(float);
