@@ -70,6 +70,7 @@ typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(8))) unsigned u32x8_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -1274,19 +1275,44 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as
 
 __global__ void zero_f32_kernel(float* p) { p[0] = 0.0f; }
 
-// max |x| over bf16 inputs, as the bit pattern of a non-negative fp32 (NaN skipped)
+// max |x| over bf16 inputs, as the bit pattern of a non-negative fp32 (NaN
+// skipped).  16-byte loads over the aligned middle, element loads for the
+// unaligned head and the tail; one atomic per workgroup, on a grid of at most
+// a few hundred workgroups, so the single target word sees little contention.
+__device__ __forceinline__ void amax_take(unsigned& m, uint32_t h) {
+  const unsigned a = (h & 0x7fffu) << 16;
+  if (a <= 0x7f800000u && a > m) m = a;
+}
+
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t n, unsigned* __restrict__ amax) {
   unsigned m = 0;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
-    const unsigned a = static_cast<unsigned>(x[i] & 0x7fffu) << 16;
-    if (a <= 0x7f800000u && a > m) m = a;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t tid = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t head = min(n, static_cast<int64_t>((16u - (reinterpret_cast<uintptr_t>(x) & 15u)) & 15u) / 2);
+  const int64_t nv = (n - head) >> 3;
+  for (int64_t i = tid; i < head; i += stride) amax_take(m, x[i]);
+  const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(x + head);
+  for (int64_t i = tid; i < nv; i += stride) {
+    const u32x4_t u = xv[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      amax_take(m, u[k] & 0xffffu);
+      amax_take(m, u[k] >> 16);
+    }
   }
+  for (int64_t i = head + 8 * nv + tid; i < n; i += stride) amax_take(m, x[i]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const unsigned v = __shfl_xor(m, o);
     m = v > m ? v : m;
   }
-  if ((threadIdx.x & 63) == 0 && m) atomicMax(amax, m);
+  __shared__ unsigned wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+    if (m) atomicMax(amax, m);
+  }
 }
 
 __global__ void fp8_scale_kernel(float* scale) {
@@ -1306,14 +1332,35 @@ __device__ __forceinline__ uint8_t to_e4m3fn(float v) {
   return static_cast<uint8_t>((__float_as_uint(v) >> 24 & 0x80u) | static_cast<unsigned>(mag));
 }
 
+__device__ __forceinline__ uint8_t quant_fp8_one(uint32_t h, float sc) {
+  float q = bf16_bits_to_f32(static_cast<uint16_t>(h)) / sc;
+  q = q > 448.0f ? 448.0f : (q < -448.0f ? -448.0f : q);
+  return to_e4m3fn(q);
+}
+
+// Eight elements per thread and step (16 bytes in, 8 out) when source and
+// destination share their offset from a 16 / 8-byte boundary; element by
+// element otherwise and for the tail.
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ scale,
-                                                        uint8_t* __restrict__ dst) {
+                                                        uint8_t* __restrict__ dst, int vec) {
   const float sc = scale[0];
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
-    float q = bf16_bits_to_f32(x[i]) / sc;
-    q = q > 448.0f ? 448.0f : (q < -448.0f ? -448.0f : q);
-    dst[i] = to_e4m3fn(q);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t tid = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t nv = vec ? n >> 3 : 0;
+  const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(x);
+  for (int64_t i = tid; i < nv; i += stride) {
+    const u32x4_t u = xv[i];
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      lo |= static_cast<uint32_t>(quant_fp8_one(u[k] & 0xffffu, sc)) << (16 * k);
+      lo |= static_cast<uint32_t>(quant_fp8_one(u[k] >> 16, sc)) << (16 * k + 8);
+      hi |= static_cast<uint32_t>(quant_fp8_one(u[k + 2] & 0xffffu, sc)) << (16 * k);
+      hi |= static_cast<uint32_t>(quant_fp8_one(u[k + 2] >> 16, sc)) << (16 * k + 8);
+    }
+    *reinterpret_cast<u32x2_t*>(dst + 8 * i) = u32x2_t{lo, hi};
   }
+  for (int64_t i = 8 * nv + tid; i < n; i += stride) dst[i] = quant_fp8_one(x[i], sc);
 }
 
 // Nearest e2m1 code to v (ties to even, saturating at 6): thresholds are the
@@ -1579,13 +1626,14 @@ int mla_quantize_fp8(const void* src_bf16, int64_t n, uint8_t* dst, float* scale
   if (dynamic) {
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(1), 0, st, scale);
     if (n > 0)
-      hipLaunchKernelGGL(amax_kernel, dim3(grid_for(n, 256 * 16)), dim3(256), 0, st, static_cast<const uint16_t*>(src_bf16), n,
-                         reinterpret_cast<unsigned*>(scale));
+      hipLaunchKernelGGL(amax_kernel, dim3(min(grid_for(n, 256 * 64), 2 * device_cus())), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(src_bf16), n, reinterpret_cast<unsigned*>(scale));
     hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(1), 0, st, scale);
   }
+  const int vec = (reinterpret_cast<uintptr_t>(src_bf16) & 15u) == 0 && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0;
   if (n > 0)
-    hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid_for(n, 256 * 8)), dim3(256), 0, st, static_cast<const uint16_t*>(src_bf16),
-                       n, scale, dst);
+    hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid_for(n, 256 * 32)), dim3(256), 0, st, static_cast<const uint16_t*>(src_bf16),
+                       n, scale, dst, vec);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 

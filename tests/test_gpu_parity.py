@@ -54,6 +54,25 @@ def test_fp8_quantizer_bit_exact(orc, seed):
     assert np.array_equal(u8(codes_g2), codes_o2)
 
 
+@pytest.mark.parametrize("x_off,d_off", [(3, 0), (0, 5), (3, 3), (8, 8), (1, 7)])
+@pytest.mark.parametrize("big_at", ["head", "tail", "middle"])
+def test_fp8_quantizer_unaligned_views(orc, x_off, d_off, big_at):
+    """Source and destination views off their 16 / 8-byte boundaries: the
+    element-wise head and tail paths of the amax and the quantiser."""
+    n = 40_003
+    x = synth.normal_bf16((n + 16,), 400 + x_off + d_off)
+    pos = {"head": x_off, "tail": x_off + n - 1, "middle": x_off + n // 2}[big_at]
+    x[pos] = -37.5
+    xs = x[x_off:x_off + n]
+    buf = torch.zeros(n + 16, dtype=torch.float8_e4m3fn, device=DEV)
+    codes_g, sc_g = mla.quantize_fp8(x.to(DEV)[x_off:x_off + n], out=buf[d_off:d_off + n])
+    codes_o, sc_o = orc.quant_fp8(bits(xs.contiguous()))
+    assert float(sc_g.item()) == sc_o == float(np.float32(37.5) / np.float32(448.0))
+    assert np.array_equal(u8(codes_g), codes_o)
+    rest = u8(buf)
+    assert not rest[:d_off].any() and not rest[d_off + n:].any()  # nothing written outside the view
+
+
 def test_mxfp4_quantizer_bit_exact(orc):
     x = synth.normal_bf16((4099, 576), 300)
     x[5] = 0.0                       # all-zero row
