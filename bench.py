@@ -81,6 +81,7 @@ def compulsory_bytes(w, page_size) -> int:
 
 def build_inputs(w, device):
     case = synth.workload_case(w, device=device)
+    mla.check_tables(case["kv_indptr"], case["page_table"], w.page_size, case["kv"].shape[0])
     B = w.batch
     ops = {"kv_indptr": case["kv_indptr"], "page_table": case["page_table"]}
     if w.kv_fmt == "fp8":
@@ -232,6 +233,7 @@ def time_ragged(steps, warmup, device, warmup_s=0.3):
     B, mean_len = 64, 8192
     lengths = synth.ragged_lengths(B, mean_len, 1.0, synth.BASE_SEED + 50)
     case = synth.make_case(B, lengths, 8, shuffle=True, seed=synth.BASE_SEED + 51, device=device)
+    mla.check_tables(case["kv_indptr"], case["page_table"], 8, case["kv"].shape[0])
     kv, ks = mla.quantize_fp8(case["kv"])
     q, ind, pt = case["q"], case["kv_indptr"], case["page_table"]
     del case
@@ -265,6 +267,7 @@ def time_multi_token(steps, warmup, device, warmup_s=0.3):
     with the 4 query groups per request counted as workgroups."""
     B, L, rows = 64, 8192, 64
     case = synth.make_case(B, L, 8, shuffle=True, seed=synth.BASE_SEED + 60, device=device)
+    mla.check_tables(case["kv_indptr"], case["page_table"], 8, case["kv"].shape[0])
     kv, ks = mla.quantize_fp8(case["kv"])
     q = synth.normal_bf16((B, rows, 576), seed=synth.BASE_SEED + 61, device=device)
     ind, pt = case["kv_indptr"], case["page_table"]
@@ -294,6 +297,7 @@ def time_mixed(steps, warmup, device, warmup_s=0.3):
     (306 B of mxfp4 K and 512 B of fp8 V per token) + Q + page table + out."""
     B, L, P = 256, 8192, 8
     case = synth.make_case(B, L, P, shuffle=True, seed=synth.BASE_SEED + 70, device=device)
+    mla.check_tables(case["kv_indptr"], case["page_table"], P, case["kv"].shape[0])
     k, ks = mla.quantize_mxfp4(case["kv"])
     v, vs = mla.quantize_fp8(case["kv"])
     qp, qe = mla.quantize_mxfp4(case["q"].reshape(B * 16, 576))

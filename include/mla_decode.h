@@ -26,7 +26,8 @@
  *     are detected on the host before anything is enqueued.  Device-resident
  *     contents (indptr monotonicity, page ids in range) are not inspected on
  *     the hot path: out-of-range page ids are undefined behaviour, exactly as
- *     for an out-of-range pointer.
+ *     for an out-of-range pointer.  mla_check_tables checks host copies of
+ *     the tables against the cache size before they are uploaded.
  *   - bf16 values are raw IEEE bfloat16 bit patterns (uint16).
  */
 #ifndef MLA_DECODE_H_
@@ -121,6 +122,29 @@ int mla_validate(const void* q, int32_t q_dtype, const void* q_scale,
                  const int32_t* kv_indptr, int32_t batch,
                  const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
                  int32_t num_splits, void* out, void* workspace, size_t workspace_bytes);
+
+/*
+ * mla_check_tables - host check of the index tables a decode call will read
+ * (pure host code, no HIP call): every token a request covers must map to a
+ * physical row inside the cache, by the paging rule given for mla_decode.
+ *
+ * kv_indptr_host   host int32[batch+1], non-negative and nondecreasing.
+ * page_table_host  host int32[page_table_len] (may be NULL when that is 0).
+ * page_indptr_host NULL (one table over the token stream) or host
+ *                  int32[batch] (per-request tables, non-negative starts).
+ * page_size        >= 1; num_kv_rows >= 0 cache rows.
+ * bad_request      optional out: the first request whose tokens fail (or -1
+ *                  for a size error or when every check passes).
+ *
+ * Returns MLA_OK; MLA_ERR_NULL for a missing table; MLA_ERR_ARG for
+ * batch < 0, page_size < 1, negative sizes, decreasing or negative offsets,
+ * a page-table index past page_table_len, or a page id whose rows fall
+ * outside [0, num_kv_rows).  Cost: one pass over the pages the requests
+ * touch.
+ */
+int mla_check_tables(const int32_t* kv_indptr_host, int32_t batch, const int32_t* page_table_host,
+                     int64_t page_table_len, const int32_t* page_indptr_host, int32_t page_size,
+                     int64_t num_kv_rows, int32_t* bad_request);
 
 /* Bytes of workspace mla_decode needs: fp32 partial outputs [batch,S,16,512]
  * plus base-2 log-sum-exps [batch,S,16]; 0 when num_splits == 1.  Returns 0

@@ -48,7 +48,7 @@ _DECODE_ARGS = [_c_void, _c_int32, _c_void, _c_void, _c_int32, _c_void, _c_int64
 EXPORTS = ("mla_decode", "mla_validate", "mla_workspace_bytes", "mla_choose_num_splits",
            "mla_recommend_page_size", "mla_quantize_fp8", "mla_quantize_mxfp4", "mla_stream_read",
            "mla_plan_worklist", "mla_worklist_workspace_bytes", "mla_decode_worklist", "mla_decode_rows",
-           "mla_workspace_bytes_rows", "mla_decode_mixed", "mla_validate_mixed",
+           "mla_workspace_bytes_rows", "mla_decode_mixed", "mla_validate_mixed", "mla_check_tables",
            "mla_status_string", "mla_abi_version")
 
 
@@ -82,6 +82,9 @@ def load():
             L.mla_quantize_fp8.argtypes = [_c_void, _c_int64, _c_void, _c_void, _c_int32, _c_void]
             L.mla_quantize_mxfp4.restype = ctypes.c_int
             L.mla_quantize_mxfp4.argtypes = [_c_void, _c_int64, _c_int64, _c_void, _c_void, _c_void]
+            L.mla_check_tables.restype = ctypes.c_int
+            L.mla_check_tables.argtypes = [_c_void, _c_int32, _c_void, ctypes.c_int64, _c_void, _c_int32,
+                                           ctypes.c_int64, _c_void]
             L.mla_plan_worklist.restype = ctypes.c_int
             L.mla_plan_worklist.argtypes = [_c_void, _c_int32, _c_int32, _c_int32, _c_void, _c_void, _c_void, _c_void]
             L.mla_worklist_workspace_bytes.restype = _c_size
@@ -370,6 +373,33 @@ def plan_worklist(kv_indptr, num_cus: int = 0, max_items: int | None = None):
     if rc:
         raise StatusError("mla_plan_worklist", rc)
     return items[: n_items.value].clone(), req[:batch].clone(), n_slots.value
+
+
+def check_tables(kv_indptr, page_table, page_size: int, num_kv_rows: int, page_indptr=None) -> None:
+    """Check host copies of the index tables against the cache (mla_check_tables).
+
+    Every token must map to a physical row in [0, num_kv_rows) under the
+    paging rule of `decode`.  Tables may be CPU tensors, numpy arrays or
+    lists (device tensors are copied to the host).  Raises ValueError naming
+    the first bad request, or StatusError for a size or argument error.
+    """
+    ind = torch.as_tensor(kv_indptr, dtype=torch.int32).detach().contiguous().cpu()
+    pt = torch.as_tensor(page_table, dtype=torch.int32).detach().contiguous().cpu().reshape(-1)
+    pi = None if page_indptr is None else torch.as_tensor(page_indptr, dtype=torch.int32).detach().contiguous().cpu()
+    batch = ind.numel() - 1
+    if batch < 0:
+        raise ValueError("kv_indptr needs at least one entry")
+    if pi is not None and pi.numel() < batch:
+        raise ValueError("page_indptr needs one entry per request")
+    bad = ctypes.c_int32(-1)
+    rc = load().mla_check_tables(ind.data_ptr(), batch, pt.data_ptr() if pt.numel() else None, pt.numel(),
+                                 None if pi is None else pi.data_ptr(), int(page_size), int(num_kv_rows),
+                                 ctypes.addressof(bad))
+    if rc and bad.value >= 0:
+        raise ValueError(f"request {bad.value}: offsets decrease or a token maps outside the page table "
+                         f"or the {num_kv_rows}-row cache")
+    if rc:
+        raise StatusError("mla_check_tables", rc)
 
 
 def worklist_workspace_bytes(num_slots: int, q_rows: int = HEADS) -> int:

@@ -124,6 +124,43 @@ int mla_validate_mixed(const void* q, int32_t q_dtype, const void* q_scale, int3
   return MLA_OK;
 }
 
+int mla_check_tables(const int32_t* kv_indptr_host, int32_t batch, const int32_t* page_table_host,
+                     int64_t page_table_len, const int32_t* page_indptr_host, int32_t page_size,
+                     int64_t num_kv_rows, int32_t* bad_request) {
+  if (bad_request) *bad_request = -1;
+  if (batch < 0 || page_size < 1 || page_table_len < 0 || num_kv_rows < 0) return MLA_ERR_ARG;
+  if (!kv_indptr_host) return MLA_ERR_NULL;
+  if (page_table_len > 0 && !page_table_host) return MLA_ERR_NULL;
+  if (kv_indptr_host[0] < 0) return MLA_ERR_ARG;
+  const int64_t P = page_size;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t g0 = kv_indptr_host[b], g1 = kv_indptr_host[b + 1];
+    auto fail = [&]() {
+      if (bad_request) *bad_request = b;
+      return MLA_ERR_ARG;
+    };
+    if (g1 < g0) return fail();
+    if (g1 == g0) continue;
+    // token t sits at position p = p0 + t of the table stream: entry p / P,
+    // row offset p % P inside that page (one shared table: p0 = g0; per
+    // request tables: p0 = page_indptr[b] * P)
+    int64_t p0 = g0;
+    if (page_indptr_host) {
+      if (page_indptr_host[b] < 0) return fail();
+      p0 = static_cast<int64_t>(page_indptr_host[b]) * P;
+    }
+    const int64_t p1 = p0 + (g1 - g0);
+    for (int64_t j = p0 / P; j <= (p1 - 1) / P; ++j) {
+      if (j >= page_table_len) return fail();
+      const int64_t pid = page_table_host[j];
+      // highest in-page offset this request uses on page j
+      const int64_t hi = (p1 - 1 < j * P + P - 1 ? p1 - 1 : j * P + P - 1) - j * P;
+      if (pid < 0 || pid * P + hi >= num_kv_rows) return fail();
+    }
+  }
+  return MLA_OK;
+}
+
 int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, int32_t num_cus) {
   if (batch < 1 || kv_len < 1) return 1;
   if (num_cus <= 0) num_cus = 256;

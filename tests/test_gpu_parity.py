@@ -106,6 +106,8 @@ def u8t(x):
 # ---------------------------------------------------------------- decode
 def prepare(case, q_fmt, kv_fmt, orc, q_static=6.0 / 448.0):
     """GPU operands (GPU quantisers) and oracle operands (oracle quantisers); asserts equal codes."""
+    mla.check_tables(case["kv_indptr"], case["page_table"], case["page_size"], case["kv"].shape[0],
+                     page_indptr=case["page_indptr"])
     kv_g = case["kv"].to(DEV)
     q_g = case["q"].to(DEV)
     g = {"page_table": case["page_table"].to(DEV), "kv_indptr": case["kv_indptr"].to(DEV),

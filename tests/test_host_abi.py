@@ -254,3 +254,70 @@ def test_split_heuristic_mixed(lib):
             assert 1 <= s <= 256 and (s == 1 or (L + s - 1) // s >= 32)
     assert mla.choose_num_splits(256, 8192, mla.MIXED) == 1
     assert mla.choose_num_splits(4, 8192, mla.MIXED) >= 16
+
+
+def _rows_in_range(indptr, table, P, nrows, page_indptr=None):
+    """Brute force: map every token by the paging rule and test its row."""
+    for b in range(len(indptr) - 1):
+        L = indptr[b + 1] - indptr[b]
+        if L < 0:
+            return False
+        for t in range(L):
+            if page_indptr is None:
+                g = indptr[b] + t
+                j, off = g // P, g % P
+            else:
+                j, off = page_indptr[b] + t // P, t % P
+            if j >= len(table) or table[j] < 0 or table[j] * P + off >= nrows:
+                return False
+    return True
+
+
+def test_check_tables_cases(lib):
+    # shared table, page 4: 22 tokens over pages 0..5, last page half used
+    ind = [0, 5, 5, 22]
+    mla.check_tables(ind, [3, 0, 4, 1, 2, 5], 4, 22)          # page 5 holds rows 20, 21 only
+    with pytest.raises(ValueError, match="request 2"):
+        mla.check_tables(ind, [3, 0, 4, 1, 5, 2], 4, 22)      # page 5 as a full page: rows 20..23
+    with pytest.raises(ValueError, match="request 2"):
+        mla.check_tables(ind, [3, 0, 4, 1, 2], 4, 22)         # table one page short
+    with pytest.raises(ValueError, match="request 0"):
+        mla.check_tables(ind, [-1, 0, 4, 1, 2, 5], 4, 22)     # negative page id
+    with pytest.raises(ValueError, match="request 1"):
+        mla.check_tables([0, 5, 4, 22], [3, 0, 4, 1, 2, 5], 4, 22)  # decreasing offsets
+    # per-request tables: request b starts at entry page_indptr[b]
+    mla.check_tables([0, 3, 9], [2, 0, 1], 4, 12, page_indptr=[0, 1])
+    with pytest.raises(ValueError, match="request 0"):
+        mla.check_tables([0, 3, 9], [2, 0, 1], 4, 10, page_indptr=[0, 1])  # request 0 reaches row 10
+    with pytest.raises(ValueError, match="request 1"):
+        mla.check_tables([0, 3, 9], [2, 0, 1], 4, 12, page_indptr=[0, 2])  # request 1 needs entry 3
+    mla.check_tables([0], [], 8, 0)                             # empty batch
+    mla.check_tables([0, 0, 0], [], 8, 0)                       # only empty requests
+    with pytest.raises(mla.StatusError):
+        mla.check_tables([0, 4], [0], 0, 8)                     # page_size 0
+    assert lib.mla_check_tables(None, 1, None, 0, None, 1, 1, None) == -1  # MLA_ERR_NULL
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_check_tables_matches_brute_force(lib, seed):
+    rng = np.random.default_rng(seed)
+    B, P = int(rng.integers(1, 5)), int(rng.integers(1, 9))
+    lens = rng.integers(0, 40, size=B)
+    per_request = bool(rng.integers(0, 2))
+    indptr = [int(rng.integers(0, 5))] + [0] * B
+    for b in range(B):
+        indptr[b + 1] = indptr[b] + int(lens[b])
+    npages = int(indptr[-1] // P + B + 8)
+    table = rng.permutation(npages).astype(np.int32)
+    page_indptr = None
+    if per_request:
+        page_indptr = [int(x) for x in rng.integers(0, npages, size=B)]
+    nrows = int(rng.integers(npages * P // 2, npages * P + 1))
+    if rng.integers(0, 4) == 0:
+        table[int(rng.integers(0, npages))] = -int(rng.integers(1, 3))
+    want = _rows_in_range(indptr, [int(x) for x in table], P, nrows, page_indptr)
+    if want:
+        mla.check_tables(indptr, table, P, nrows, page_indptr=page_indptr)
+    else:
+        with pytest.raises(ValueError):
+            mla.check_tables(indptr, table, P, nrows, page_indptr=page_indptr)
