@@ -35,7 +35,8 @@ class Workload:
 
 
 # The five benchmark shapes (bs x kv_len x precision mix) plus the bs=256 fp8
-# shape, the long-context HBM-bound headline case.
+# shape, the long-context HBM-bound headline case, with bf16 Q and with Q
+# quantised to fp8 under the static 6/448 scale.
 WORKLOADS = {
     w.name: w
     for w in [
@@ -46,6 +47,7 @@ WORKLOADS = {
         Workload("bs256_kv8192_mxfp4", 256, 8192, "bf16", "mxfp4", 8, True, 2, None, 4),
         Workload("bs256_kv8192_mxfp4_q4", 256, 8192, "mxfp4", "mxfp4", 8, True, 2, None, 5),
         Workload("bs256_kv8192_a16w8", 256, 8192, "bf16", "fp8", 8, True, None, None, 6),
+        Workload("bs256_kv8192_a8w8", 256, 8192, "fp8", "fp8", 8, True, None, 6.0 / 448.0, 7),
     ]
 }
 
