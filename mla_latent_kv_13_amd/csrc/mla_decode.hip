@@ -327,6 +327,13 @@ __device__ __forceinline__ f32x4_t mfma_fp4(i32x4_t a, uint32_t sa, i32x4_t b, u
 }
 
 __device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
+// three-input maximum of values that are never NaN (logits and -inf), as one
+// instruction: written out because fmaxf would first quiet each input
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with
 // gfx950's cross-row swaps: VALU-only, no LDS round trip.
@@ -880,12 +887,17 @@ void stage1_kernel(Stage1Args a) {
     float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = (4 * g + r < ntok) ? s0[r] * c_log2 : -__builtin_huge_valf();
-      sv[4 + r] = (16 + 4 * g + r < ntok) ? s1[r] * c_log2 : -__builtin_huge_valf();
+      sv[r] = s0[r] * c_log2;
+      sv[4 + r] = s1[r] * c_log2;
     }
-    float mx = sv[0];
+    if (ntok < kSub) {  // wave-uniform: only a range's last sub-tile is short
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmax3(mx, sv[i]);
+      for (int r = 0; r < 4; ++r) {
+        if (4 * g + r >= ntok) sv[r] = -__builtin_huge_valf();
+        if (16 + 4 * g + r >= ntok) sv[4 + r] = -__builtin_huge_valf();
+      }
+    }
+    float mx = vmax3(vmax3(sv[0], sv[1], sv[2]), vmax3(sv[3], sv[4], sv[5]), fmax3(sv[6], sv[7]));
     mx = group_max(mx);
 #pragma unroll
     for (int c = 0; c < 32; c += 8) pin_acc8(acc + c);
