@@ -913,11 +913,13 @@ void stage1_kernel(Stage1Args a) {
     }
     u32x4_t pw;
     float psum = 0.0f;
+    const bf16x2_t kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bf16x2_t pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i] - m_run)),
                            static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i + 1] - m_run))};
-      psum += static_cast<float>(pr.x) + static_cast<float>(pr.y);
+      // the running sum takes the same bf16-rounded weights the MFMA sees
+      psum = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, psum, false);
       pw[i] = bits(pr);
     }
     l_run += psum;
