@@ -216,9 +216,10 @@ __device__ __forceinline__ void pin8(T* v) {
 }
 
 
-// 2^(e-127), exact for every code including e = 0 (a denormal)
+// 2^(e-127), exact for every code including e = 0 (a denormal): one ldexp
+// of the constant 2^-127
 __device__ __forceinline__ float e8m0_f32(uint32_t e) {
-  return __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(e) - 127);
+  return __builtin_amdgcn_ldexpf(0x1p-127f, static_cast<int>(e));
 }
 
 __device__ __forceinline__ uint32_t bits(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
@@ -528,6 +529,11 @@ void stage1_kernel(Stage1Args a) {
   const uint32_t gbase = a.page_indptr ? static_cast<uint32_t>(t0) : static_cast<uint32_t>(kv0 + t0);
   const int32_t* ptab = a.page_table + (a.page_indptr ? a.page_indptr[b] : 0);
   const uint32_t P = static_cast<uint32_t>(a.page_size);
+  // page index and slot of a stream position: shifts for power-of-two page
+  // sizes (wave-uniform branch), a division otherwise
+  const int plog = (P & (P - 1u)) == 0u ? __builtin_ctz(P) : -1;
+  auto page_of = [&](uint32_t gp) { return plog >= 0 ? gp >> plog : gp / P; };
+  auto slot_of = [&](uint32_t gp) { return plog >= 0 ? gp & (P - 1u) : gp % P; };
 
   // ---- per-wave LDS ring
   const uint32_t wbase = smem0 + static_cast<uint32_t>(w) * L::kWaveBytes;
@@ -541,7 +547,7 @@ void stage1_kernel(Stage1Args a) {
     const int xc = X < nloc ? X : (nloc > 0 ? nloc - 1 : 0);
     const int tok = min(kSub * (w + kWaves * xc) + (lane & 31), max(n - 1, 0));
     const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
-    dma_b32(ptab + gpos / P, pid_addr(X));
+    dma_b32(ptab + page_of(gpos), pid_addr(X));
   };
   constexpr int U = Kv<KF>::kUnits;
   // Per DMA instruction i, this lane fills LDS chunk 64i + lane = token t,
@@ -612,7 +618,7 @@ void stage1_kernel(Stage1Args a) {
       const int tok = ub + min(lane, nv - 1);
       const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
       const uint32_t pid = static_cast<uint32_t>(lds_ld<int>(static_cast<int>(pid_addr(X)) + 4 * lane));
-      row = pid * P + gpos % P;
+      row = pid * P + slot_of(gpos);
       lds_st<uint32_t>(rt + 4 * lane, row);
       lds_st<uint64_t>(pt + 8 * lane, reinterpret_cast<uint64_t>(a.kv + static_cast<int64_t>(row) * ROW));
       if constexpr (KF == FMIX)
@@ -836,15 +842,18 @@ void stage1_kernel(Stage1Args a) {
           c0[c] = lds_ld<uint8_t>(sb0 + 4 * c + g);
           c1[c] = lds_ld<uint8_t>(sb1 + 4 * c + g);
         }
-        u0[4] = i32x4_t{0, 0, 0, 0};
-        u1[4] = u0[4];
-        c0[4] = 127u;
-        c1[4] = 127u;
-        if (g < 2) {
-          u0[4] = lds_ld<i32x4_t>(tb + 16 * (tq0 * UK + 16 + g));
-          u1[4] = lds_ld<i32x4_t>(tb + 16 * (tq1 * UK + 16 + g));
-          c0[4] = lds_ld<uint8_t>(sb0 + 16 + g);
-          c1[4] = lds_ld<uint8_t>(sb1 + 16 + g);
+        // dims 576..639 (lane groups 2 and 3 of the fifth chunk) are
+        // padding: Q is zero there, and e2m1 codes are always finite, so
+        // whatever the LDS holds past the row (the next row, or the wave's
+        // scale area after the last slot) adds exactly zero.  Only the block
+        // scale must stay finite: 2^0.
+        u0[4] = lds_ld<i32x4_t>(tb + 16 * (tq0 * UK + 16 + g));
+        u1[4] = lds_ld<i32x4_t>(tb + 16 * (tq1 * UK + 16 + g));
+        c0[4] = lds_ld<uint8_t>(sb0 + 16 + g);
+        c1[4] = lds_ld<uint8_t>(sb1 + 16 + g);
+        if (g >= 2) {
+          c0[4] = 127u;
+          c1[4] = 127u;
         }
         sched_fence();
         if constexpr (kSplitQ) {
