@@ -532,8 +532,20 @@ void stage1_kernel(Stage1Args a) {
   // page index and slot of a stream position: shifts for power-of-two page
   // sizes (wave-uniform branch), a division otherwise
   const int plog = (P & (P - 1u)) == 0u ? __builtin_ctz(P) : -1;
-  auto page_of = [&](uint32_t gp) { return plog >= 0 ? gp >> plog : gp / P; };
-  auto slot_of = [&](uint32_t gp) { return plog >= 0 ? gp & (P - 1u) : gp % P; };
+  // (the opaque copy of P keeps the compiler from hoisting the division's
+  // reciprocal out of the loop and then computing both forms every sub-tile)
+  auto page_of = [&](uint32_t gp) -> uint32_t {
+    if (plog >= 0) return gp >> plog;
+    uint32_t p = P;
+    asm volatile("" : "+s"(p));
+    return gp / p;
+  };
+  auto slot_of = [&](uint32_t gp) -> uint32_t {
+    if (plog >= 0) return gp & (P - 1u);
+    uint32_t p = P;
+    asm volatile("" : "+s"(p));
+    return gp % p;
+  };
 
   // ---- per-wave LDS ring
   const uint32_t wbase = smem0 + static_cast<uint32_t>(w) * L::kWaveBytes;
