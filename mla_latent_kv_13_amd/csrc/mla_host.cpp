@@ -32,10 +32,13 @@ int64_t kv_row_bytes(int32_t kd) {
 
 namespace {
 // Measured fastest split counts on the 8-shape grid, written by
-// mla_latent_kv_13_amd/tune_splits.py.
+// mla_latent_kv_13_amd/tune_splits.py, with the cost model's own pick and its
+// measured time beside each (a record of how close the fallback model is).
 struct SplitEntry {
   int32_t batch, kv_len, kv_dtype, splits;
   double us;
+  int32_t model_splits;
+  double model_us;
 };
 constexpr SplitEntry kSplitTable[] = {
 #include "split_table.inc"
