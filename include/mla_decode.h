@@ -159,8 +159,9 @@ size_t mla_workspace_bytes(int32_t batch, int32_t num_splits);
  * mla_latent_kv_13_amd/tune_splits.py.  Elsewhere an occupancy cost model
  * decides: ceil(batch*S / num_cus) rounds of one workgroup per CU, each
  * streaming its chunk rounded up to 128 tokens, plus for S > 1 the partial
- * outputs, a second launch and a per-split stage-2 latency; the model alone
- * reproduces every tuned optimum of the grid.  (Page 695854's split selectors
+ * outputs, a second launch and a per-split stage-2 latency; on the grid the
+ * model alone picks the tuned optimum on all shapes but one near-tie, and its
+ * pick there measured within 6 % of it.  (Page 695854's split selectors
  * and page 668813's split tables pick S per shape for the same reasons.)
  * Returns a value in 1..MLA_MAX_SPLITS; pure host code.
  */
