@@ -134,6 +134,36 @@ def test_split_table_is_used_and_matched_by_the_model(lib):
     assert agree >= 22
 
 
+def test_split_table_rebuild_from_log(lib, tmp_path):
+    """The tuner's offline path: a sweep log becomes a table whose rows hold
+    the fastest split count and the cost model's own pick with its time."""
+    from mla_latent_kv_13_amd import tune_splits as ts
+
+    log = tmp_path / "sweep.jsonl"
+    with open(log, "w") as f:
+        f.write("not json: a warning line the tuner skips\n")
+        for batch in ts.BATCHES:
+            for kv_len in ts.KV_LENS:
+                for fmt, code in ts.FORMATS:
+                    model = ts.model_splits(batch, kv_len, code)
+                    for s in sorted(set(ts.SPLITS) | {model}):
+                        # a synthetic timing with its minimum at S = 2
+                        us = 10.0 + abs(s - 2)
+                        f.write(f'{{"batch": {batch}, "kv_len": {kv_len}, "kv": "{fmt}", "splits": {s}, "us": {us}}}\n')
+    out = tmp_path / "table.inc"
+    rows = ts.from_log(str(log), str(out))
+    assert len(rows) == 24
+    text = open(out).read()
+    parsed = [tuple(float(x) for x in m.groups())
+              for m in re.finditer(r"\{(\d+), (\d+), (\d+), (\d+), ([0-9.]+), (\d+), ([0-9.]+)\}", text)]
+    assert len(parsed) == 24
+    for (batch, kv_len, code, s, us, model_s, model_us), row in zip(parsed, rows):
+        assert (int(batch), int(kv_len), int(code)) == row[:3]
+        assert int(s) == 2 and us == 10.0
+        assert int(model_s) == ts.model_splits(int(batch), int(kv_len), int(code))
+        assert model_us == 10.0 + abs(model_s - 2)
+
+
 def test_stream_read_argument_errors(lib):
     # every one of these is rejected (or is a no-op) before anything is launched
     assert lib.mla_stream_read(A, 0, A2, None) == 0
