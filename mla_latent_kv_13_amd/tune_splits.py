@@ -148,8 +148,9 @@ def _write(out_path, rows, where):
             f.write(f"{{{batch}, {kv_len}, {code}, {s}, {us:.2f}, {model}, {model_us:.2f}}},  // {fmt}\n")
 
 
-def from_log(log_path, out_path):
-    """Rebuild the table from the JSON lines of an earlier GPU run (no GPU)."""
+def from_log(log_path, out_path, where=None):
+    """Rebuild the table from the JSON lines of an earlier GPU run (no GPU);
+    `where` names that run (device and date) in the table's header."""
     timed = {}
     for line in open(log_path):
         if not line.startswith("{"):
@@ -166,7 +167,7 @@ def from_log(log_path, out_path):
                 if model not in t:
                     raise SystemExit(f"the log has no timing of the model's pick S={model} for {(batch, kv_len, fmt)}")
                 rows.append(_row(batch, kv_len, fmt, t, model))
-    _write(out_path, rows, f"the GPU run logged in {os.path.basename(log_path)}")
+    _write(out_path, rows, where or f"the GPU run logged in {os.path.basename(log_path)}")
     return rows
 
 
@@ -174,10 +175,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=None, help="write the C table here")
     ap.add_argument("--from-log", default=None, help="rebuild the table from this run's JSON lines (no GPU)")
+    ap.add_argument("--where", default=None, help="with --from-log: the device and date of that run, for the header")
     args = ap.parse_args()
     if args.from_log:
         load()
-        from_log(args.from_log, args.out)
+        from_log(args.from_log, args.out, args.where)
         return
     if not torch.cuda.is_available():
         print("tune_splits needs a GPU", file=sys.stderr)
