@@ -202,6 +202,39 @@ def test_decode_matches_oracle(orc, qf, kf, shape):
             assert not out[b].any()
 
 
+def random_case_params(i):
+    """Seeded random decode configuration: batch, ragged lengths (with empty
+    and one-token requests), page size (powers of two and not), paging
+    convention, split count and format pair."""
+    rng = np.random.default_rng(7000 + i)
+    batch = int(rng.integers(1, 7))
+    lengths = []
+    for _ in range(batch):
+        u = rng.random()
+        lengths.append(0 if u < 0.12 else 1 if u < 0.24 else int(rng.integers(2, 2500)))
+    P = int(rng.choice([1, 2, 3, 5, 8, 16, 32]))
+    per_req = bool(rng.random() < 0.5)
+    S = int(rng.choice([1, 2, 3, 4, 5, 8, 13, 16, 32, 64]))
+    qf, kf = PAIRS[int(rng.integers(0, len(PAIRS)))]
+    return lengths, P, per_req, S, qf, kf
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_random_configurations(orc, i):
+    """Thirty seeded random configurations against the oracle, element-wise."""
+    lengths, P, per_req, S, qf, kf = random_case_params(i)
+    print(f"[random {i}] q={qf} kv={kf} lengths={lengths} P={P} S={S} per_request={per_req}", flush=True)
+    case = synth.make_case(len(lengths), lengths, P, shuffle=True, seed=7100 + i, per_request_pages=per_req,
+                           extra_pages=1)
+    g, o = prepare(case, qf, kf, orc)
+    out = gpu_decode(case, g, S)
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what=f"random {i}: {qf}/{kf} P={P} S={S}")
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert not out[b].any()
+
+
 @pytest.mark.parametrize("kf", ["bf16", "fp8", "mxfp4"])
 def test_split_count_invariance(orc, kf):
     case = synth.make_case(3, [700, 129, 1], 8, shuffle=True, seed=500)
