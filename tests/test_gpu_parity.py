@@ -235,6 +235,32 @@ def test_random_configurations(orc, i):
             assert not out[b].any()
 
 
+@pytest.mark.parametrize("i", range(12))
+def test_random_worklist_rows(orc, i):
+    """Seeded random work-list decodes with 16 to 64 query rows per request:
+    a random planner CU count, ragged lengths, page size and paging."""
+    rng = np.random.default_rng(7300 + i)
+    lengths, P, per_req, _, qf, kf = random_case_params(100 + i)
+    rows = int(rng.choice([16, 32, 48, 64]))
+    cus = int(rng.choice([4, 16, 64, 256]))
+    print(f"[random worklist {i}] q={qf} kv={kf} rows={rows} cus={cus} lengths={lengths} P={P} "
+          f"per_request={per_req}", flush=True)
+    case = synth.make_case(len(lengths), lengths, P, shuffle=True, seed=7400 + i, per_request_pages=per_req)
+    case["q"] = synth.normal_bf16((len(lengths), rows, 576), seed=7500 + i)
+    g, o = prepare(case, qf, kf, orc)
+    items, req, ns = mla.plan_worklist(case["kv_indptr"].cpu(), num_cus=cus)
+    out = mla.decode_worklist(g["q"], g["kv"], g["kv_indptr"], g["page_table"], case["page_size"], items.to(DEV),
+                              req.to(DEV), ns, q_scale=g["q_scale"], kv_scale=g["kv_scale"],
+                              page_indptr=g["page_indptr"])
+    torch.cuda.synchronize()
+    assert out.shape == (len(lengths), rows, 512)
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what=f"random worklist {i}: {qf}/{kf} rows={rows} cus={cus}")
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert not out[b].any()
+
+
 @pytest.mark.parametrize("kf", ["bf16", "fp8", "mxfp4"])
 def test_split_count_invariance(orc, kf):
     case = synth.make_case(3, [700, 129, 1], 8, shuffle=True, seed=500)
