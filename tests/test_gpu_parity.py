@@ -650,6 +650,24 @@ def test_mixed_matches_oracle(orc, qf, shape):
             assert not out[b].any()
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_random_mixed(orc, i):
+    """Seeded random decodes over the split cache (mxfp4 K, fp8 V from
+    independent data), bf16 or mxfp4 Q."""
+    lengths, P, per_req, S, _, _ = random_case_params(200 + i)
+    qf = "bf16" if i % 2 == 0 else "mxfp4"
+    print(f"[random mixed {i}] q={qf} lengths={lengths} P={P} S={S} per_request={per_req}", flush=True)
+    case = synth.make_case(len(lengths), lengths, P, shuffle=True, seed=7600 + i, per_request_pages=per_req,
+                           extra_pages=1)
+    g, o, _ = prepare_mixed(case, qf, orc, v_seed=7700 + i)
+    out = gpu_decode_mixed(case, g, S)
+    ref, _ = oracle_mixed(case, o, orc)
+    check_close(out, ref, what=f"random mixed {i}: {qf} P={P} S={S}")
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert not out[b].any()
+
+
 @pytest.mark.parametrize("S", [1, 2, 3, 8, 32, 256])
 def test_mixed_split_count_invariance(orc, S):
     case = synth.make_case(3, [700, 129, 1], 8, shuffle=True, seed=960)
