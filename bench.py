@@ -72,11 +72,15 @@ def measured_traffic(workload: str):
 
 
 def compulsory_bytes(w, page_size) -> int:
+    """Bytes one call must move at least: cache rows (with mxfp4 scale rows),
+    Q (with its scales), the fp32 per-tensor scales of fp8 operands, the page
+    table, kv_indptr and the bf16 output."""
     T = w.batch * w.kv_len
     kv = {"bf16": 1152, "fp8": 576, "mxfp4": 288 + 18}[w.kv_fmt] * T
     q = {"bf16": 2 * 576, "fp8": 576, "mxfp4": 288 + 18}[w.q_fmt] * w.batch * 16
+    scales = 4 * ((w.kv_fmt == "fp8") + (w.q_fmt == "fp8"))
     pt = 4 * math.ceil(T / page_size)
-    return kv + q + pt + 4 * (w.batch + 1) + 2 * w.batch * 16 * 512
+    return kv + q + scales + pt + 4 * (w.batch + 1) + 2 * w.batch * 16 * 512
 
 
 def build_inputs(w, device):

@@ -1,0 +1,47 @@
+"""The benchmark's byte accounting: compulsory bytes per call of every
+workload, written out term by term from the layouts (cache rows of 1152 /
+576 / 288 + 18 bytes, Q rows, fp32 per-tensor scales, 4-byte page ids,
+kv_indptr and the [batch, 16, 512] bf16 output)."""
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import bench  # noqa: E402
+from mla_latent_kv_13_amd import synth  # noqa: E402
+
+
+def by_hand(batch, kv_len, kv_row, q_row, n_scales, page_size):
+    tokens = batch * kv_len
+    pages = -(-tokens // page_size)
+    return (tokens * kv_row + batch * 16 * q_row + 4 * n_scales + 4 * pages + 4 * (batch + 1)
+            + 2 * batch * 16 * 512)
+
+
+EXPECTED = {
+    # workload: (kv row bytes, Q row bytes, fp32 scales, value)
+    "bs4_kv1024_bf16": (1152, 1152, 0, 4_874_260),
+    "bs32_kv1024_a16w8": (576, 1152, 1, 20_119_688),
+    "bs4_kv8192_a8w8": (576, 576, 2, 18_993_180),
+    "bs64_kv8192_a16w8": (576, 1152, 1, 304_480_520),
+    "bs256_kv8192_mxfp4": (306, 1152, 0, 651_691_012),
+    "bs256_kv8192_mxfp4_q4": (306, 306, 0, 648_225_796),
+    "bs256_kv8192_a16w8": (576, 1152, 1, 1_217_922_056),
+    "bs256_kv8192_a8w8": (576, 576, 2, 1_215_562_764),
+}
+
+
+def test_compulsory_bytes_of_every_workload():
+    assert set(EXPECTED) == set(synth.WORKLOADS)
+    for name, (kv_row, q_row, n_scales, value) in EXPECTED.items():
+        w = synth.WORKLOADS[name]
+        hand = by_hand(w.batch, w.kv_len, kv_row, q_row, n_scales, w.page_size)
+        assert hand == value, name
+        assert bench.compulsory_bytes(w, w.page_size) == value, name
+
+
+def test_headline_floor_and_target():
+    # at 8 TB/s the headline's bytes take 152.2 us; 70 % of the peak is 217.5 us
+    b = bench.compulsory_bytes(synth.WORKLOADS["bs256_kv8192_a16w8"], 8)
+    assert round(b / 8e12 * 1e6, 1) == 152.2
+    assert round(b / (0.7 * 8e12) * 1e6, 1) == 217.5
