@@ -328,6 +328,14 @@ __device__ __forceinline__ f32x4_t mfma_fp4(i32x4_t a, uint32_t sa, i32x4_t b, u
 }
 
 __device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
+// bit t of pm (t < 32), kept opaque so that the caller's doubling stays a
+// v_lshl_add: the compiler otherwise folds (pm >> t) & 1 feeding a shifted
+// add into three instructions in place of v_bfe_u32 + v_lshl_add_u32
+__device__ __forceinline__ uint32_t bit_of(uint32_t pm, int t) {
+  uint32_t b = (pm >> t) & 1u;
+  asm("" : "+v"(b));
+  return b;
+}
 // three-input maximum of values that are never NaN (logits and -inf), as one
 // instruction: written out because fmaxf would first quiet each input
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
@@ -842,8 +850,8 @@ void stage1_kernel(Stage1Args a) {
         }
       }
     } else {  // mxfp4 K: block scales read once per (token, block)
-      const int sb0 = static_cast<int>(sc_addr(x)) + 20 * tq0 + 2 * ((pmask >> tq0) & 1u);
-      const int sb1 = static_cast<int>(sc_addr(x)) + 20 * tq1 + 2 * ((pmask >> tq1) & 1u);
+      const int sb0 = static_cast<int>(sc_addr(x)) + 20 * tq0 + 2 * static_cast<int>(bit_of(pmask, tq0));
+      const int sb1 = static_cast<int>(sc_addr(x)) + 20 * tq1 + 2 * static_cast<int>(bit_of(pmask, tq1));
       {
         i32x4_t u0[5], u1[5];
         uint32_t c0[5], c1[5];
@@ -1010,7 +1018,7 @@ void stage1_kernel(Stage1Args a) {
         vw[kk][1] = u.y;
         vw[kk][2] = u.z;
         vw[kk][3] = u.w;
-        const int sa = sbase + 2 * static_cast<int>(__builtin_amdgcn_ubfe(pl, dt, 1));
+        const int sa = sbase + 2 * static_cast<int>(bit_of(pl, dt));
         vsc[kk] = e8m0_f32(lds_ld<uint8_t>(sa + 20 * dt));
       }
       sched_fence();
