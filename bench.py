@@ -183,7 +183,7 @@ def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
     reps = replicate(ops, nrep)
     for r in reps:
         r["out"] = torch.empty((w.batch, 16, 512), dtype=torch.bfloat16, device=device)
-        r["ws"] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device) if ws_bytes else None
+        r["ws"] = mla.new_workspace(ws_bytes, device)
 
     def caller(nsplit, nr):
         def call(i):
@@ -244,8 +244,7 @@ def time_ragged(steps, warmup, device, warmup_s=0.3):
     S = mla.choose_num_splits(B, mean_len, mla.FP8)
     items, req, ns = mla.plan_worklist(ind.cpu())
     items_d, req_d = items.to(device), req.to(device)
-    ws = torch.empty(max(16, mla.workspace_bytes(B, S), mla.worklist_workspace_bytes(ns)), dtype=torch.uint8,
-                     device=device)
+    ws = mla.new_workspace(max(mla.workspace_bytes(B, S), mla.worklist_workspace_bytes(ns)), device)
     out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=device)
     uni = time_calls(lambda i: mla.decode(q, kv, ind, pt, 8, S, kv_scale=ks, out=out, workspace=ws), steps, warmup,
                      warmup_s)[0]
@@ -277,7 +276,7 @@ def time_multi_token(steps, warmup, device, warmup_s=0.3):
     ind, pt = case["kv_indptr"], case["page_table"]
     del case
     S = mla.choose_num_splits(B * rows // 16, L, mla.FP8)
-    ws = torch.empty(max(16, mla.workspace_bytes(B, S, rows)), dtype=torch.uint8, device=device)
+    ws = mla.new_workspace(mla.workspace_bytes(B, S, rows), device)
     out = torch.empty((B, rows, 512), dtype=torch.bfloat16, device=device)
     ms = time_calls(lambda i: mla.decode(q, kv, ind, pt, 8, S, kv_scale=ks, out=out, workspace=ws), steps, warmup,
                     warmup_s)[0]
@@ -310,8 +309,7 @@ def time_mixed(steps, warmup, device, warmup_s=0.3):
     del case
     torch.cuda.empty_cache()
     S_h = mla.choose_num_splits(B, L, mla.MIXED)
-    ws = torch.empty(max(16, mla.workspace_bytes(B, 2), mla.workspace_bytes(B, S_h)), dtype=torch.uint8,
-                     device=device)
+    ws = mla.new_workspace(max(mla.workspace_bytes(B, 2), mla.workspace_bytes(B, S_h)), device)
     out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=device)
     ms2 = time_calls(lambda i: mla.decode_mixed(q, k, ks, v, vs, ind, pt, P, 2, q_scale=qe, out=out, workspace=ws),
                      steps, warmup, warmup_s)[0]

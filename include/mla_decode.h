@@ -24,10 +24,13 @@
  *     Work is enqueued on it; nothing synchronises with the host.
  *   - Return value: MLA_OK (0) or a negative MLA_ERR_* code.  Argument errors
  *     are detected on the host before anything is enqueued.  Device-resident
- *     contents (indptr monotonicity, page ids in range) are not inspected on
- *     the hot path: out-of-range page ids are undefined behaviour, exactly as
- *     for an out-of-range pointer.  mla_check_tables checks host copies of
- *     the tables against the cache size before they are uploaded.
+ *     contents (indptr monotonicity, page ids in range) are not checked on the
+ *     hot path: a gathered row past the cache is clamped to its last row (so
+ *     a corrupt page id gives wrong values, never an access outside the
+ *     cache), while kv_indptr / page_indptr entries that index past the page
+ *     table are undefined behaviour, as for an out-of-range pointer.
+ *     mla_check_tables checks host copies of the tables against the cache
+ *     size before they are uploaded.
  *   - bf16 values are raw IEEE bfloat16 bit patterns (uint16).
  */
 #ifndef MLA_DECODE_H_

@@ -29,7 +29,7 @@ __all__ = [
     "BF16", "FP8", "MXFP4", "HEADS", "D_QK", "D_V",
     "load", "decode", "workspace_bytes", "choose_num_splits", "recommend_page_size",
     "quantize_fp8", "quantize_mxfp4", "validate", "status_string", "StatusError",
-    "mxfp4_scale_buffer", "MIXED", "decode_mixed", "validate_mixed",
+    "mxfp4_scale_buffer", "MIXED", "decode_mixed", "validate_mixed", "new_workspace",
 ]
 
 BF16, FP8, MXFP4 = 0, 1, 2
@@ -150,12 +150,41 @@ def workspace_bytes(batch: int, num_splits: int, q_rows: int = HEADS) -> int:
     return int(load().mla_workspace_bytes_rows(int(batch), int(q_rows), int(num_splits)))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor | None:
+    """A workspace of nbytes on `device` (None for 0 bytes)."""
+    if nbytes <= 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
 def choose_num_splits(batch: int, kv_len: int, kv_dtype: int, num_cus: int = 0) -> int:
     return int(load().mla_choose_num_splits(int(batch), int(kv_len), int(kv_dtype), int(num_cus)))
 
 
 def recommend_page_size(batch: int, kv_len: int) -> int:
     return int(load().mla_recommend_page_size(int(batch), int(kv_len)))
+
+
+def _check_operands(q, kv_cache, kv_scale, out, batch: int, rows: int, what: str = "kv_cache") -> None:
+    """Shape and dtype checks the C ABI cannot make from raw pointers (it
+    would read or write past a wrong-sized buffer): Q rows, cache row width,
+    the padded mxfp4 scale allocation, and the output tensor."""
+    fmt = _fmt(kv_cache)
+    width = MXFP4_ROW_BYTES if fmt == MXFP4 else D_QK
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != width:
+        raise ValueError(f"{what} must be [rows, {width}] for its format, got {tuple(kv_cache.shape)}")
+    if q.dim() != 3 or q.shape[0] != batch or q.shape[2] != (MXFP4_ROW_BYTES if _fmt(q) == MXFP4 else D_QK):
+        raise ValueError(f"q must be [batch, rows, 576] (mxfp4: [batch, rows, 288]), got {tuple(q.shape)}")
+    if fmt == MXFP4 and kv_scale is not None:
+        need = (MXFP4_ROW_SCALES * kv_cache.shape[0] + 15) // 16 * 16
+        have = kv_scale.untyped_storage().nbytes() - kv_scale.storage_offset() * kv_scale.element_size()
+        if kv_scale.dtype != torch.uint8 or kv_scale.numel() < MXFP4_ROW_SCALES * kv_cache.shape[0] or have < need:
+            raise ValueError(f"mxfp4 scales need {MXFP4_ROW_SCALES} uint8 per row in an allocation of at least "
+                             f"{need} bytes (mxfp4_scale_buffer)")
+    if fmt == FP8 and kv_scale is not None and (kv_scale.dtype != torch.float32 or kv_scale.numel() < 1):
+        raise ValueError("the fp8 cache scale is a 1-element float32 tensor")
+    if out is not None and (out.dtype != torch.bfloat16 or tuple(out.shape) != (batch, rows, D_V)):
+        raise ValueError(f"out must be bfloat16 [{batch}, {rows}, {D_V}], got {out.dtype} {tuple(out.shape)}")
 
 
 def _decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale, kv_scale,
@@ -187,6 +216,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
     """
     batch = kv_indptr.numel() - 1
     rows = _q_rows(q, batch)
+    _check_operands(q, kv_cache, kv_scale, out, batch, rows)
     if num_splits is None:
         # one workgroup per 16-row query group: the occupancy is batch x groups
         hint = kv_len_hint if kv_len_hint is not None else max(1, kv_cache.shape[0] // max(batch, 1))
@@ -194,9 +224,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
     if out is None:
         out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=kv_cache.device)
     if workspace is None and batch > 0:
-        need = workspace_bytes(batch, num_splits, rows)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=kv_cache.device)
+        workspace = new_workspace(workspace_bytes(batch, num_splits, rows), kv_cache.device)
     _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out, workspace)
     args = _decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale, kv_scale, page_indptr,
                         out, workspace)
@@ -242,15 +270,16 @@ def decode_mixed(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, 
     """
     batch = kv_indptr.numel() - 1
     rows = _q_rows(q, batch)
+    _check_operands(q, k_cache, k_scale, out, batch, rows, "k_cache")
+    if v_cache.dim() != 2 or v_cache.shape[1] != D_QK:
+        raise ValueError(f"v_cache must be [rows, {D_QK}], got {tuple(v_cache.shape)}")
     if num_splits is None:
         hint = kv_len_hint if kv_len_hint is not None else max(1, k_cache.shape[0] // max(batch, 1))
         num_splits = choose_num_splits(batch * (rows // HEADS), hint, MIXED)
     if out is None:
         out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=k_cache.device)
     if workspace is None and batch > 0:
-        need = workspace_bytes(batch, num_splits, rows)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=k_cache.device)
+        workspace = new_workspace(workspace_bytes(batch, num_splits, rows), k_cache.device)
     _dev(q, k_cache, k_scale, v_cache, v_scale, kv_indptr, page_table, q_scale, page_indptr, out, workspace)
     if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.float8_e4m3fn:
         raise TypeError("decode_mixed takes a uint8 mxfp4 key cache and a float8_e4m3fn value cache")
@@ -412,10 +441,11 @@ def decode_worklist(q, kv_cache, kv_indptr, page_table, page_size, items, req, n
     device copies of plan_worklist's tensors.  Returns out [batch,16,512] bf16."""
     batch = kv_indptr.numel() - 1
     rows = _q_rows(q, batch)
+    _check_operands(q, kv_cache, kv_scale, out, batch, rows)
     if out is None:
         out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=kv_cache.device)
     if workspace is None and num_slots > 0:
-        workspace = torch.empty(worklist_workspace_bytes(num_slots, rows), dtype=torch.uint8, device=kv_cache.device)
+        workspace = new_workspace(worklist_workspace_bytes(num_slots, rows), kv_cache.device)
     _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out, workspace, items, req)
     args = _decode_args(q, kv_cache, kv_indptr, page_table, page_size, 1, q_scale, kv_scale, page_indptr, out,
                         workspace)

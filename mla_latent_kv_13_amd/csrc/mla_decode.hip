@@ -383,6 +383,7 @@ struct Stage1Args {
   int32_t units;         // (request, split) pairs or work items
   int32_t page_size;
   int32_t num_splits;
+  uint32_t max_row;      // last physical cache row: gathered rows are clamped to it
   float sm_scale_log2e;
 };
 
@@ -638,7 +639,9 @@ void stage1_kernel(Stage1Args a) {
       const int tok = ub + min(lane, nv - 1);
       const uint32_t gpos = gbase + static_cast<uint32_t>(tok);
       const uint32_t pid = static_cast<uint32_t>(lds_ld<int>(static_cast<int>(pid_addr(X)) + 4 * lane));
-      row = pid * P + slot_of(gpos);
+      // a page id past the cache (a corrupt table) reads the last row rather
+      // than memory outside the cache
+      row = min(pid * P + slot_of(gpos), a.max_row);
       lds_st<uint32_t>(rt + 4 * lane, row);
       lds_st<uint64_t>(pt + 8 * lane, reinterpret_cast<uint64_t>(a.kv + static_cast<int64_t>(row) * ROW));
       if constexpr (KF == FMIX)
@@ -1589,6 +1592,7 @@ int decode_launch(const void* q, int32_t q_dtype, const void* q_scale, int32_t q
   a.units = static_cast<int32_t>(units);
   a.page_size = page_size;
   a.num_splits = items ? 1 : num_splits;
+  a.max_row = static_cast<uint32_t>(std::min<int64_t>(num_kv_rows - 1, 0xffffffffLL));
   a.sm_scale_log2e = static_cast<float>(1.4426950408889634 / 24.0);  // log2(e) / sqrt(576)
   const int64_t grid = G == 1 ? units : (units + 7) / 8 * 8 * G;
   // more workgroups than CUs: two-wave workgroups, two per CU, one round

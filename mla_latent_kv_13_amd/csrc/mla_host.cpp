@@ -63,18 +63,21 @@ const char* mla_status_string(int status) {
   }
 }
 
+namespace {
+// partial outputs (16-byte aligned rows), then the log-sum-exps, for `parts`
+// partial rows of 512 values
+size_t workspace_for_parts(size_t parts) { return parts * MLA_HEAD_DIM_V * sizeof(float) + parts * sizeof(float); }
+}  // namespace
+
 size_t mla_workspace_bytes_rows(int32_t batch, int32_t q_rows, int32_t num_splits) {
   if (q_rows < MLA_NUM_HEADS || q_rows % MLA_NUM_HEADS || q_rows > MLA_MAX_Q_ROWS) return 0;
-  const size_t per16 = mla_workspace_bytes(batch, num_splits);
-  return per16 / MLA_NUM_HEADS * q_rows;
+  if (batch < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return 0;
+  if (num_splits == 1) return 0;
+  return workspace_for_parts(static_cast<size_t>(batch) * static_cast<size_t>(num_splits) * q_rows);
 }
 
 size_t mla_workspace_bytes(int32_t batch, int32_t num_splits) {
-  if (batch < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return 0;
-  if (num_splits == 1) return 0;
-  const size_t parts = static_cast<size_t>(batch) * static_cast<size_t>(num_splits) * MLA_NUM_HEADS;
-  // partial outputs first (16-byte aligned rows), then the log-sum-exps
-  return parts * MLA_HEAD_DIM_V * sizeof(float) + parts * sizeof(float);
+  return mla_workspace_bytes_rows(batch, MLA_NUM_HEADS, num_splits);
 }
 
 int mla_validate(const void* q, int32_t q_dtype, const void* q_scale, const void* kv_cache,
@@ -85,7 +88,8 @@ int mla_validate(const void* q, int32_t q_dtype, const void* q_scale, const void
   (void)page_indptr;  // optional
   if (batch < 0) return MLA_ERR_ARG;
   if (page_size < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_ARG;
-  if (num_kv_rows < 0) return MLA_ERR_ARG;
+  // rows are indexed with 32-bit arithmetic on the device
+  if (num_kv_rows < 0 || num_kv_rows > 0xffffffffLL) return MLA_ERR_ARG;
   if (static_cast<int64_t>(batch) * num_splits > 0x7fffffffLL) return MLA_ERR_ARG;
   if (!supported_pair(q_dtype, kv_dtype)) return MLA_ERR_DTYPE;
   if (batch == 0) return MLA_OK;  // nothing to do
@@ -269,8 +273,7 @@ int mla_plan_worklist(const int32_t* kv_indptr_host, int32_t batch, int32_t num_
 
 size_t mla_worklist_workspace_bytes(int32_t num_slots, int32_t q_rows) {
   if (num_slots <= 0 || q_rows < MLA_NUM_HEADS || q_rows % MLA_NUM_HEADS || q_rows > MLA_MAX_Q_ROWS) return 0;
-  const size_t parts = static_cast<size_t>(num_slots) * q_rows;
-  return parts * MLA_HEAD_DIM_V * sizeof(float) + parts * sizeof(float);
+  return workspace_for_parts(static_cast<size_t>(num_slots) * q_rows);
 }
 
 int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len) {

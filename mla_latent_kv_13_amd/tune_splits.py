@@ -32,7 +32,8 @@ import time
 
 import torch
 
-from . import BF16, FP8, MXFP4, choose_num_splits, decode, load, quantize_fp8, quantize_mxfp4, workspace_bytes
+from . import (BF16, FP8, MXFP4, choose_num_splits, decode, load, new_workspace, quantize_fp8, quantize_mxfp4,
+               workspace_bytes)
 from . import synth
 
 BATCHES = (4, 32, 64, 256)
@@ -112,7 +113,7 @@ def tune(out_path: str | None):
                     d = base if r == 0 else {k: (None if v is None else v.clone()) for k, v in base.items()}
                     d = dict(d)
                     d["out"] = torch.empty((batch, 16, 512), dtype=torch.bfloat16, device="cuda")
-                    d["ws"] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+                    d["ws"] = new_workspace(ws_bytes, "cuda")
                     reps.append(d)
                 model = model_splits(batch, kv_len, code)
                 timed = {}

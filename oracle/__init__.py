@@ -16,6 +16,7 @@ Parity status of each entry point (pins live in ``tests/test_oracle_*.py``):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -39,6 +40,9 @@ BF16, FP8, MXFP4 = 0, 1, 2
 _DTYPES = {"bf16": BF16, "fp8": FP8, "mxfp4": MXFP4}
 
 
+_CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math", "-ffp-contract=off"]
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into _build/liboracle.so with gcc (OpenMP, no fast-math)."""
     os.makedirs(_BUILD, exist_ok=True)
@@ -46,11 +50,44 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(src):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-           "-ffp-contract=off", src, "-o", tmp, "-lm"]
-    subprocess.run(cmd, check=True)
+    subprocess.run(["gcc", *_CFLAGS, src, "-o", tmp, "-lm"], check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def source() -> str:
+    """The text of oracle.c (the mutation tests patch a copy of it)."""
+    with open(os.path.join(_HERE, "oracle.c")) as f:
+        return f.read()
+
+
+def build_variant(text: str, path: str, extra_flags=()) -> str:
+    """Compile C text (a patched copy of oracle.c) with the oracle's own flags
+    into the shared library `path`; test infrastructure for mutation tests and
+    sanitizer builds."""
+    d = os.path.dirname(os.path.abspath(path))
+    os.makedirs(d, exist_ok=True)
+    src = os.path.splitext(path)[0] + ".c"
+    with open(src, "w") as f:
+        f.write(text)
+    subprocess.run(["gcc", *_CFLAGS, *extra_flags, src, "-o", path, "-lm"], check=True)
+    return path
+
+
+@contextlib.contextmanager
+def variant(path: str):
+    """Route every call of this module to the library at `path` (a variant
+    built by build_variant) inside the with-block, then restore the oracle."""
+    global _lib
+    lib()
+    with _lock:
+        saved = _lib
+        _lib = _configure(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        with _lock:
+            _lib = saved
 
 
 class _Problem(ctypes.Structure):
@@ -77,37 +114,38 @@ class _Problem(ctypes.Structure):
     ]
 
 
+def _configure(L):
+    L.orc_bf16_to_f64.restype = ctypes.c_double
+    L.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    L.orc_e4m3fn_to_f64.restype = ctypes.c_double
+    L.orc_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+    L.orc_e2m1_to_f64.restype = ctypes.c_double
+    L.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+    L.orc_e8m0_to_f64.restype = ctypes.c_double
+    L.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+    L.orc_f64_to_bf16.restype = ctypes.c_uint16
+    L.orc_f64_to_bf16.argtypes = [ctypes.c_double]
+    L.orc_amax_bf16.restype = ctypes.c_float
+    L.orc_amax_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    L.orc_fp8_scale_from_amax.restype = ctypes.c_float
+    L.orc_fp8_scale_from_amax.argtypes = [ctypes.c_float]
+    L.orc_quant_fp8.restype = ctypes.c_int
+    L.orc_quant_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
+    L.orc_quant_mxfp4.restype = ctypes.c_int
+    L.orc_quant_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    L.orc_decode.restype = ctypes.c_int
+    L.orc_decode.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32, ctypes.c_void_p,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
+    return L
+
+
 def lib():
     global _lib
     with _lock:
         if _lib is None:
             build(force=False)  # compiles only when missing or older than oracle.c
-            L = ctypes.CDLL(_LIB_PATH)
-            L.orc_bf16_to_f64.restype = ctypes.c_double
-            L.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
-            L.orc_e4m3fn_to_f64.restype = ctypes.c_double
-            L.orc_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
-            L.orc_e2m1_to_f64.restype = ctypes.c_double
-            L.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
-            L.orc_e8m0_to_f64.restype = ctypes.c_double
-            L.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
-            L.orc_f64_to_bf16.restype = ctypes.c_uint16
-            L.orc_f64_to_bf16.argtypes = [ctypes.c_double]
-            L.orc_amax_bf16.restype = ctypes.c_float
-            L.orc_amax_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64]
-            L.orc_fp8_scale_from_amax.restype = ctypes.c_float
-            L.orc_fp8_scale_from_amax.argtypes = [ctypes.c_float]
-            L.orc_quant_fp8.restype = ctypes.c_int
-            L.orc_quant_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
-            L.orc_quant_mxfp4.restype = ctypes.c_int
-            L.orc_quant_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
-                                          ctypes.c_void_p, ctypes.c_void_p]
-            L.orc_set_mutation.restype = None
-            L.orc_set_mutation.argtypes = [ctypes.c_int]
-            L.orc_decode.restype = ctypes.c_int
-            L.orc_decode.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32, ctypes.c_void_p,
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
-            _lib = L
+            _lib = _configure(ctypes.CDLL(_LIB_PATH))
     return _lib
 
 
@@ -192,11 +230,6 @@ def quant_mxfp4(bits):
 
 
 # ------------------------------------------------------------------ decode
-
-def set_mutation(m: int) -> None:
-    """Plant one of the oracle.c mistakes (tests only); 0 restores the oracle."""
-    lib().orc_set_mutation(int(m))
-
 
 def decode(q, kv, kv_indptr, page_table, page_size, *, q_dtype="bf16", kv_dtype="bf16",
            q_scale=1.0, q_e8m0=None, kv_scale=1.0, kv_e8m0=None, page_indptr=None,

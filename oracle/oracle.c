@@ -75,17 +75,6 @@
 enum { ORC_BF16 = 0, ORC_FP8 = 1, ORC_MXFP4 = 2 };
 enum { ORC_OK = 0, ORC_EARG = -1, ORC_EINDEX = -2, ORC_ENOMEM = -3 };
 
-/* Planted-mistake switch for the pin tests only (0 = the correct oracle).
- * Each value breaks one thing a real implementation could get wrong, so a
- * test can show that at least one pin catches it:
- *   1 drop the rope term from the logits     2 scale 1/sqrt(512) instead of 1/sqrt(576)
- *   3 read the next physical row             4 take V from dims 64..575
- *   5 use the neighbouring head's query      6 negate the logits
- *   7 swap the two nibbles of an mxfp4 byte  8 leave kv_scale off V
- *   9 take V from the key cache when a separate value cache is given      */
-static int g_mutation = 0;
-void orc_set_mutation(int m) { g_mutation = m; }
-
 /* ---------------------------------------------------------------- codecs */
 
 double orc_bf16_to_f64(uint16_t h) {
@@ -277,8 +266,7 @@ static void deq_row(int dtype, const void* base, int64_t row, double scale, cons
     const uint8_t* s = e8m0 + row * ORC_NBLK;
     for (int i = 0; i < ORC_DQK; i++) {
       uint8_t byte = p[i / 2];
-      int hi = (i & 1) ^ (g_mutation == 7);
-      uint8_t nib = hi ? (byte >> 4) : (byte & 15);
+      uint8_t nib = (i & 1) ? (byte >> 4) : (byte & 15);
       out[i] = orc_e2m1_to_f64(nib) * orc_e8m0_to_f64(s[i / 32]);
     }
   }
@@ -293,7 +281,6 @@ static int64_t phys_row(const orc_problem* P, int b, int64_t t) {
   if (idx < 0 || idx >= P->page_table_len) return -1;
   int64_t pg = P->page_table[idx];
   int64_t row = pg * P->page_size + g % P->page_size;
-  if (g_mutation == 3 && row + 1 < P->kv_rows) row += 1;
   if (pg < 0 || row < 0 || row >= P->kv_rows) return -1;
   return row;
 }
@@ -330,6 +317,13 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
   int64_t npairs = sel ? nsel : (int64_t)P->batch * rows;
   int bad = 0;
   if (nthreads <= 0) nthreads = 1;
+  /* source of V: the separate value cache when one is given */
+  const int sep_v = P->v != NULL;
+  const int v_dtype = sep_v ? P->v_dtype : P->kv_dtype;
+  const void* v_src = sep_v ? P->v : P->kv;
+  const double v_scale = sep_v ? P->v_scale : P->kv_scale;
+  const uint8_t* v_e8m0 = sep_v ? NULL : P->kv_e8m0;
+  const double inv_sqrt = 1.0 / sqrt((double)ORC_DQK);
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
   for (int64_t pi = 0; pi < npairs; pi++) {
     int b = sel ? sel[2 * pi] : (int)(pi / rows);
@@ -340,7 +334,7 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
     }
     int64_t L = (int64_t)P->kv_indptr[b + 1] - P->kv_indptr[b];
     double q[ORC_DQK], k[ORC_DQK];
-    int64_t qrow = (int64_t)b * rows + (g_mutation == 5 ? (h ^ 1) : h);
+    int64_t qrow = (int64_t)b * rows + h;
     deq_row(P->q_dtype, P->q, qrow, P->q_scale, P->q_e8m0, q);
     double* o = (double*)calloc(ORC_DV, sizeof(double));
     double* s = (double*)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
@@ -350,32 +344,39 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
       bad |= 4;
       continue;
     }
-    const double inv_sqrt = (g_mutation == 6 ? -1.0 : 1.0) / sqrt(g_mutation == 2 ? 512.0 : (double)ORC_DQK);
-    const int qk_dims = g_mutation == 1 ? ORC_DV : ORC_DQK;
-    const int v0 = g_mutation == 4 ? 64 : 0;
-    /* source of V: the separate value cache when one is given */
-    const int sep_v = P->v != NULL && g_mutation != 9;
-    const int v_dtype = sep_v ? P->v_dtype : P->kv_dtype;
-    const double v_scale = sep_v ? P->v_scale : P->kv_scale;
-    const double v_fix = (g_mutation == 8 && v_dtype == ORC_FP8) ? 1.0 / v_scale : 1.0;
-    /* logits */
-    for (int64_t t = 0; t < L && !bad; t++) {
+    /* logits; a token outside the page table or the cache fails this pair */
+    int pair_err = 0;
+    for (int64_t t = 0; t < L; t++) {
       int64_t row = phys_row(P, b, t);
       if (row < 0) {
-        bad |= 2;
+        pair_err = 1;
         break;
       }
       deq_row(P->kv_dtype, P->kv, row, P->kv_scale, P->kv_e8m0, k);
       double dot = 0.0;
-      for (int i = 0; i < qk_dims; i++) dot += q[i] * k[i];
+      for (int i = 0; i < ORC_DQK; i++) dot += q[i] * k[i];
       s[t] = dot * inv_sqrt;
     }
-    if (!(bad & 2) && L > 0) {
+    if (pair_err) {
+      bad |= 2;
+      free(o);
+      free(s);
+      continue;
+    }
+    if (L > 0) {
       int S = num_splits == 0 ? 1 : num_splits;
       int64_t chunk = (L + S - 1) / S;
       double Mx = -INFINITY;
       double* lse = (double*)malloc(sizeof(double) * S);
       double* os = (double*)calloc((size_t)S * ORC_DV, sizeof(double));
+      if (!lse || !os) {
+        free(lse);
+        free(os);
+        free(o);
+        free(s);
+        bad |= 4;
+        continue;
+      }
       for (int sp = 0; sp < S; sp++) {
         int64_t t0 = (int64_t)sp * chunk, t1 = t0 + chunk < L ? t0 + chunk : L;
         lse[sp] = -INFINITY;
@@ -387,12 +388,8 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
         for (int64_t t = t0; t < t1; t++) {
           double p = exp(s[t] - m);
           l += p;
-          int64_t row = phys_row(P, b, t);
-          if (sep_v)
-            deq_row(v_dtype, P->v, row, v_scale, NULL, k);
-          else
-            deq_row(P->kv_dtype, P->kv, row, P->kv_scale, P->kv_e8m0, k);
-          for (int i = 0; i < ORC_DV; i++) os[(size_t)sp * ORC_DV + i] += p * k[v0 + i] * v_fix;
+          deq_row(v_dtype, v_src, phys_row(P, b, t), v_scale, v_e8m0, k);
+          for (int i = 0; i < ORC_DV; i++) os[(size_t)sp * ORC_DV + i] += p * k[i];
         }
         for (int i = 0; i < ORC_DV; i++) os[(size_t)sp * ORC_DV + i] /= l;
         lse[sp] = m + log(l);
@@ -409,12 +406,10 @@ int orc_decode(const orc_problem* P, int32_t num_splits, double* out_f64, uint16
       free(lse);
       free(os);
     }
-    if (!(bad & 2)) {
-      for (int i = 0; i < ORC_DV; i++) {
-        size_t idx = ((size_t)b * rows + h) * ORC_DV + i;
-        if (out_f64) out_f64[idx] = o[i];
-        if (out_bf16) out_bf16[idx] = orc_f64_to_bf16(o[i]);
-      }
+    for (int i = 0; i < ORC_DV; i++) {
+      size_t idx = ((size_t)b * rows + h) * ORC_DV + i;
+      if (out_f64) out_f64[idx] = o[i];
+      if (out_bf16) out_bf16[idx] = orc_f64_to_bf16(o[i]);
     }
     free(o);
     free(s);

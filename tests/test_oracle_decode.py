@@ -13,13 +13,16 @@
   rows): torch SDPA with separately dequantised K and V, one token gives that
   token's fp8 value row exactly, and identical keys give the mean of the fp8
   value rows.
-* Planted mistakes (oracle.c's mutation switch) each fail at least one pin.
+* Planted mistakes (patched copies of oracle.c, tests/oracle_mutants.py) each
+  fail at least one pin.
 """
 import numpy as np
 import pytest
 import torch
 
 from mla_latent_kv_13_amd import synth
+
+from oracle_mutants import MUTANTS, mutant_source
 
 E2M1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
 
@@ -283,7 +286,6 @@ PINS = {
 
 @pytest.mark.parametrize("name", sorted(PINS))
 def test_pin(orc, name):
-    orc.set_mutation(0)
     assert PINS[name](orc)
 
 
@@ -314,14 +316,27 @@ def test_selected_pairs_match_full(orc):
     assert np.isnan(part[0, 0]).all()
 
 
-@pytest.mark.parametrize("mutation", range(1, 10))
-def test_planted_mistake_fails_a_pin(orc, mutation):
-    try:
-        orc.set_mutation(mutation)
+@pytest.fixture(scope="module")
+def mutant_libs(orc, tmp_path_factory):
+    d = tmp_path_factory.mktemp("mutants")
+    text = orc.source()
+    return {name: orc.build_variant(mutant_source(text, name), str(d / f"liborc_{name}.so")) for name in MUTANTS}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistake_fails_a_pin(orc, mutant_libs, mutant):
+    with orc.variant(mutant_libs[mutant]):
         failed = [n for n, f in PINS.items() if not f(orc)]
-    finally:
-        orc.set_mutation(0)
-    assert failed, f"mutation {mutation} passed every pin"
+    assert failed, f"mutant {mutant} ({MUTANTS[mutant][0]}) passed every pin"
+
+
+def test_shipped_oracle_has_no_planted_mistake(orc):
+    """The mutants exist only as patches: the oracle source holds none of
+    their replacement text."""
+    text = orc.source()
+    for name, (_, patches) in MUTANTS.items():
+        for old, new in patches:
+            assert text.count(old) == 1 and new not in text, name
 
 
 def test_multi_row_equals_row_slices(orc):
