@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 /* Fixed MLA geometry (page 668813 module constants). */
 #define MLA_NUM_HEADS 16
@@ -156,25 +156,31 @@ size_t mla_workspace_bytes(int32_t batch, int32_t num_splits);
 
 /*
  * mla_choose_num_splits - split count for `batch` requests of about
- * `kv_len` tokens on a device with `num_cus` compute units (0 = 256, MI355X).
- * On the tuned grid (batch 4/32/64/256 x kv_len 1024/8192 x each cache
- * format, MI355X) it returns the measured fastest S, from a table written by
- * mla_latent_kv_13_amd/tune_splits.py.  Elsewhere an occupancy cost model
- * decides: ceil(batch*S / num_cus) rounds of one workgroup per CU, each
+ * `kv_len` tokens with Q in q_dtype over a cache in kv_dtype (any MLA_DTYPE_*
+ * code, or MLA_KV_MXFP4_K_FP8_V for the split cache; unknown codes count as
+ * bf16 Q / fp8 cache) on a device with `num_cus` compute units (0 = 256,
+ * MI355X).  On the tuned grid (batch 4/32/64/256 x kv_len 1024/8192 x the five
+ * supported format pairs, MI355X) it returns the measured fastest S, from a
+ * table written by mla_latent_kv_13_amd/tune.py.  Elsewhere an occupancy cost
+ * model decides: ceil(batch*S / num_cus) rounds of one workgroup per CU, each
  * streaming its chunk rounded up to 128 tokens, plus for S > 1 the partial
- * outputs, a second launch and a per-split stage-2 latency; on the grid the
- * model alone picks the tuned optimum on all shapes but one near-tie, and its
- * pick there measured within 6 % of it.  (Page 695854's split selectors
- * and page 668813's split tables pick S per shape for the same reasons.)
- * Returns a value in 1..MLA_MAX_SPLITS; pure host code.
+ * outputs, a second launch and a per-split stage-2 latency.  (Page 695854's
+ * split selectors and page 668813's split tables pick S per shape for the
+ * same reasons.)  Returns a value in 1..MLA_MAX_SPLITS; pure host code.
  */
-int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, int32_t num_cus);
+int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t q_dtype, int32_t kv_dtype, int32_t num_cus);
 
-/* mla_recommend_page_size - page size for a cache serving `batch` requests
- * of about `kv_len` tokens (page 668813's page-size table and page 600081's
- * selector use 1 for short and 8 for long sequences); the kernels accept any
- * page size >= 1. */
-int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len);
+/*
+ * mla_recommend_page_size - page size for a cache serving `batch` requests of
+ * about `kv_len` tokens, Q in q_dtype over a cache in kv_dtype, on `num_cus`
+ * compute units (0 = 256).  On the tuned grid (as mla_choose_num_splits) it
+ * returns the measured fastest page size of {1, 2, 4, ..., 64}; elsewhere a
+ * model: the largest power of two up to 16 that is at most a quarter of
+ * kv_len.  (Page 668813's page-size table and page 600081's selector pick 1
+ * for short and 8 for long sequences.)  The kernels accept any page size
+ * >= 1; pure host code.
+ */
+int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len, int32_t q_dtype, int32_t kv_dtype, int32_t num_cus);
 
 /*
  * mla_decode_rows - mla_decode for q_rows query rows per request: q_seq_len

@@ -75,9 +75,9 @@ def load():
             L.mla_workspace_bytes.restype = _c_size
             L.mla_workspace_bytes.argtypes = [_c_int32, _c_int32]
             L.mla_choose_num_splits.restype = _c_int32
-            L.mla_choose_num_splits.argtypes = [_c_int32, _c_int32, _c_int32, _c_int32]
+            L.mla_choose_num_splits.argtypes = [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]
             L.mla_recommend_page_size.restype = _c_int32
-            L.mla_recommend_page_size.argtypes = [_c_int32, _c_int32]
+            L.mla_recommend_page_size.argtypes = [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]
             L.mla_quantize_fp8.restype = ctypes.c_int
             L.mla_quantize_fp8.argtypes = [_c_void, _c_int64, _c_void, _c_void, _c_int32, _c_void]
             L.mla_quantize_mxfp4.restype = ctypes.c_int
@@ -157,12 +157,14 @@ def new_workspace(nbytes: int, device) -> torch.Tensor | None:
     return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
 
 
-def choose_num_splits(batch: int, kv_len: int, kv_dtype: int, num_cus: int = 0) -> int:
-    return int(load().mla_choose_num_splits(int(batch), int(kv_len), int(kv_dtype), int(num_cus)))
+def choose_num_splits(batch: int, kv_len: int, kv_dtype: int, num_cus: int = 0, *, q_dtype: int = BF16) -> int:
+    """Split count for batch requests of about kv_len tokens (mla_choose_num_splits)."""
+    return int(load().mla_choose_num_splits(int(batch), int(kv_len), int(q_dtype), int(kv_dtype), int(num_cus)))
 
 
-def recommend_page_size(batch: int, kv_len: int) -> int:
-    return int(load().mla_recommend_page_size(int(batch), int(kv_len)))
+def recommend_page_size(batch: int, kv_len: int, q_dtype: int = BF16, kv_dtype: int = FP8, num_cus: int = 0) -> int:
+    """Page size for a cache of such requests (mla_recommend_page_size)."""
+    return int(load().mla_recommend_page_size(int(batch), int(kv_len), int(q_dtype), int(kv_dtype), int(num_cus)))
 
 
 def _check_operands(q, kv_cache, kv_scale, out, batch: int, rows: int, what: str = "kv_cache") -> None:
@@ -220,7 +222,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
     if num_splits is None:
         # one workgroup per 16-row query group: the occupancy is batch x groups
         hint = kv_len_hint if kv_len_hint is not None else max(1, kv_cache.shape[0] // max(batch, 1))
-        num_splits = choose_num_splits(batch * (rows // HEADS), hint, _fmt(kv_cache))
+        num_splits = choose_num_splits(batch * (rows // HEADS), hint, _fmt(kv_cache), q_dtype=_fmt(q))
     if out is None:
         out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=kv_cache.device)
     if workspace is None and batch > 0:
@@ -275,7 +277,7 @@ def decode_mixed(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, 
         raise ValueError(f"v_cache must be [rows, {D_QK}], got {tuple(v_cache.shape)}")
     if num_splits is None:
         hint = kv_len_hint if kv_len_hint is not None else max(1, k_cache.shape[0] // max(batch, 1))
-        num_splits = choose_num_splits(batch * (rows // HEADS), hint, MIXED)
+        num_splits = choose_num_splits(batch * (rows // HEADS), hint, MIXED, q_dtype=_fmt(q))
     if out is None:
         out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=k_cache.device)
     if workspace is None and batch > 0:

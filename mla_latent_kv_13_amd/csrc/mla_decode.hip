@@ -490,6 +490,18 @@ void stage1_kernel(Stage1Args a) {
         qraw[4 * c + j] = u32x4_t{0u, 0u, 0u, 0u};
         if (d < kDqk) qraw[4 * c + j] = *reinterpret_cast<const u32x4_t*>(qrow + d);
       }
+  }
+  // Over the bf16 cache, Q is loaded after the first tiles' DMAs are issued
+  // (below): Q does not feed the gather chain (kv_indptr -> page ids ->
+  // tiles), and a wait for the page ids also waits for every load issued
+  // before them (loads complete in issue order), so loading Q late lets its
+  // latency overlap the 36 KB tiles' instead of delaying the page-id wait.
+  // The smaller fp8 and mxfp4 tiles arrive before a late Q would (measured
+  // 0.5 - 1.5 us slower there), so those formats load Q first, beside the
+  // kv_indptr -> page-id chain.
+  constexpr bool kLateQ = KF == FBF16;
+  auto load_q = [&]() {
+  if constexpr (kSplitQ) {
   } else if constexpr (QF == FBF16) {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
 #pragma unroll
@@ -500,7 +512,6 @@ void stage1_kernel(Stage1Args a) {
     for (int c = 0; c < 4; ++c) q8[c] = *reinterpret_cast<const i32x8_t*>(qrow + 128 * c + 32 * g);
     q8[4] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
     if (g < 2) q8[4] = *reinterpret_cast<const i32x8_t*>(qrow + 512 + 32 * g);
-    qs = *static_cast<const float*>(a.q_scale);
   } else {
     const size_t qr = static_cast<size_t>(v) * kHeads + hq;
     const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + qr * MLA_MXFP4_ROW_BYTES;
@@ -517,6 +528,24 @@ void stage1_kernel(Stage1Args a) {
       q4s[4] = qsc[16 + g];
     }
   }
+  };
+  // The compiler waits for the Q loads at these pins (everything issued
+  // before them completes first), so no explicit vmcnt wait of the pipeline
+  // below ever counts a Q load.
+  auto pin_q = [&]() {
+  if constexpr (QF == FBF16 && !kSplitQ) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(qb[m]));
+  } else if constexpr (QF == FFP8) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q8[m]));
+  } else if constexpr (QF == FMX) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q4[m]), "+v"(q4s[m]));
+  }
+  };
+  if constexpr (!kLateQ) load_q();
+  if constexpr (QF == FFP8) qs = *static_cast<const float*>(a.q_scale);
   if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
   float vs = 1.0f;  // split cache: V scale, applied with the final division
   if constexpr (KF == FMIX) vs = *a.kv2_scale;
@@ -574,10 +603,11 @@ void stage1_kernel(Stage1Args a) {
   // Per DMA instruction i, this lane fills LDS chunk 64i + lane = token t,
   // stored unit k (stream unit k ^ tswz(t)), packed as (8t << 16) | 16*(stream
   // unit): the row-pointer table offset and the byte offset inside the row.
-  // Every cache format keeps these in registers (bf16 36, split cache 25,
-  // fp8 18, mxfp4 9 per lane); the path that recomputes them from an opaque
-  // lane index serves any layout with more instructions per sub-tile.
-  constexpr bool kPre = Kv<KF>::kNdmaX4 <= 36;
+  // The split cache (25), fp8 (18) and mxfp4 (9 per lane) keep these in
+  // registers; bf16 rows (36 instructions) recompute them from an opaque lane
+  // index each sub-tile: 36 more live registers beside its 18 Q fragments
+  // made the compiler spill inside the loop.
+  constexpr bool kPre = Kv<KF>::kNdmaX4 <= 25;
   auto dma_pack = [](int i, int ln) {
     if constexpr (KF == FMIX) {
       // K rows: chunks 64i + ln of an 18-unit row-major stream; V rows: 32
@@ -705,7 +735,8 @@ void stage1_kernel(Stage1Args a) {
     }
   };
 
-  // The first page-id gathers overlap the Q loads; one wait covers both.
+  // The first page-id gathers (overlapping the Q loads of the formats that
+  // issue them first, which one wait covers too).
   if (nloc > 0) {
 #pragma unroll
     for (int X = 0; X < D; ++X) issue_pid(X);
@@ -713,23 +744,17 @@ void stage1_kernel(Stage1Args a) {
 
   const float c_log2 = a.sm_scale_log2e * qs * ks;
   const float out_mul = KF == FFP8 ? ks : KF == FMIX ? vs : 1.0f;
-  // Wait for the page ids and Q together, and make the compiler see Q as
-  // complete here, so its own wait for Q cannot drain the in-flight tiles later.
+  // Wait for the page ids and an early Q together, and make the compiler see
+  // that Q as complete here, so its own wait for Q cannot drain the
+  // in-flight tiles later.
   wait_vm<0>();
   if constexpr (kSplitQ) {
     // split after the first tile DMAs are issued (below): it then overlaps
     // their latency instead of delaying them
 #pragma unroll
     for (int i = 0; i < 4 * NQ; ++i) asm volatile("" : "+v"(qraw[i]));
-  } else if constexpr (QF == FBF16) {
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(qb[m]));
-  } else if constexpr (QF == FFP8) {
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q8[m]));
-  } else {
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) asm volatile("" : "+v"(q4[m]), "+v"(q4s[m]));
+  } else if constexpr (!kLateQ) {
+    pin_q();
   }
 
   // ---- running softmax state (head hq) and the O^T accumulators
@@ -1065,6 +1090,9 @@ void stage1_kernel(Stage1Args a) {
     if constexpr (kSplitQ) {
 #pragma unroll
       for (int c = 0; c < NQ; ++c) split_q_fp8(qraw + 4 * c, g, q8[c], ql[c], qhs[c], qls[c]);
+    } else if constexpr (kLateQ) {
+      load_q();
+      pin_q();
     }
     int xs = 0;  // slot of tile jx
     for (int jx = 0; jx < nloc; ++jx) {

@@ -31,18 +31,30 @@ int64_t kv_row_bytes(int32_t kd) {
 }  // namespace
 
 namespace {
-// Measured fastest split counts on the 8-shape grid, written by
-// mla_latent_kv_13_amd/tune_splits.py, with the cost model's own pick and its
-// measured time beside each (a record of how close the fallback model is).
-struct SplitEntry {
-  int32_t batch, kv_len, kv_dtype, splits;
+// Measured fastest (split count, page size) on the 8-shape grid for every
+// (Q, cache) format pair, written by mla_latent_kv_13_amd/tune.py, with the
+// cost models' own picks and their measured time beside each (a record of
+// how close the fallback models are).
+struct TuneEntry {
+  int32_t batch, kv_len, q_dtype, kv_dtype, splits, page_size;
   double us;
-  int32_t model_splits;
+  int32_t model_splits, model_page_size;
   double model_us;
 };
-constexpr SplitEntry kSplitTable[] = {
-#include "split_table.inc"
+constexpr TuneEntry kTuneTable[] = {
+#include "tune_table.inc"
 };
+
+// The tuned entry of a grid shape on a 256-CU device (MI355X), or NULL.
+const TuneEntry* tuned(int32_t batch, int32_t kv_len, int32_t q_dtype, int32_t kv_dtype, int32_t num_cus) {
+  if (num_cus != 256) return nullptr;
+  for (const TuneEntry& e : kTuneTable)
+    if (e.batch == batch && e.kv_len == kv_len && e.q_dtype == q_dtype && e.kv_dtype == kv_dtype) return &e;
+  return nullptr;
+}
+
+int32_t valid_q(int32_t q) { return q == MLA_DTYPE_FP8_E4M3FN || q == MLA_DTYPE_MXFP4 ? q : MLA_DTYPE_BF16; }
+int32_t valid_kv(int32_t kv) { return kv < MLA_DTYPE_BF16 || kv > MLA_KV_MXFP4_K_FP8_V ? MLA_DTYPE_FP8_E4M3FN : kv; }
 }  // namespace
 
 extern "C" {
@@ -168,15 +180,13 @@ int mla_check_tables(const int32_t* kv_indptr_host, int32_t batch, const int32_t
   return MLA_OK;
 }
 
-int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t kv_dtype, int32_t num_cus) {
+int32_t mla_choose_num_splits(int32_t batch, int32_t kv_len, int32_t q_dtype, int32_t kv_dtype, int32_t num_cus) {
   if (batch < 1 || kv_len < 1) return 1;
   if (num_cus <= 0) num_cus = 256;
-  if (kv_dtype < MLA_DTYPE_BF16 || kv_dtype > MLA_KV_MXFP4_K_FP8_V) kv_dtype = MLA_DTYPE_FP8_E4M3FN;
+  q_dtype = valid_q(q_dtype);
+  kv_dtype = valid_kv(kv_dtype);
   // Shapes of the tuned grid (MI355X, 256 CUs) take the measured optimum.
-  if (num_cus == 256) {
-    for (const SplitEntry& e : kSplitTable)
-      if (e.batch == batch && e.kv_len == kv_len && e.kv_dtype == kv_dtype) return e.splits;
-  }
+  if (const TuneEntry* e = tuned(batch, kv_len, q_dtype, kv_dtype, num_cus)) return e->splits;
   // Cost in "bytes streamed by the busiest CU": stage 1 runs in
   // ceil(batch*S / num_cus) rounds of one workgroup per CU, each streaming
   // its chunk rounded up to 128 tokens (four waves x 32-token sub-tiles);
@@ -276,9 +286,19 @@ size_t mla_worklist_workspace_bytes(int32_t num_slots, int32_t q_rows) {
   return workspace_for_parts(static_cast<size_t>(num_slots) * q_rows);
 }
 
-int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len) {
-  (void)batch;
-  return kv_len > 1024 ? 8 : 1;
+int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len, int32_t q_dtype, int32_t kv_dtype, int32_t num_cus) {
+  if (batch < 1 || kv_len < 1) return 1;
+  if (num_cus <= 0) num_cus = 256;
+  q_dtype = valid_q(q_dtype);
+  kv_dtype = valid_kv(kv_dtype);
+  if (const TuneEntry* e = tuned(batch, kv_len, q_dtype, kv_dtype, num_cus)) return e->page_size;
+  // Model: pages long enough that a 32-token sub-tile gathers few separate
+  // runs (each DMA instruction then reads long contiguous runs of rows and
+  // the table costs one 4-byte id per page), but no longer than a quarter of
+  // a request, so a request's last page wastes little of the cache.
+  int32_t p = 1;
+  while (p < 16 && 4 * (2 * p) <= kv_len) p *= 2;
+  return p;
 }
 
 }  // extern "C"

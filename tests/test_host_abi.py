@@ -38,7 +38,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
 
 
 def v(lib, q=A, qd=mla.BF16, qs=None, kv=A, kd=mla.BF16, ks=None, rows=100, ind=A, batch=4, pt=A,
@@ -97,71 +97,89 @@ def test_status_strings(lib):
 def test_split_heuristic(lib):
     for batch in (1, 4, 32, 64, 256, 1000):
         for L in (1, 31, 1024, 8192, 100000):
-            for kd in (mla.BF16, mla.FP8, mla.MXFP4):
-                s = mla.choose_num_splits(batch, L, kd)
+            for qd, kd in ((mla.BF16, mla.BF16), (mla.BF16, mla.FP8), (mla.FP8, mla.FP8), (mla.BF16, mla.MXFP4),
+                           (mla.MXFP4, mla.MXFP4)):
+                s = mla.choose_num_splits(batch, L, kd, q_dtype=qd)
                 assert 1 <= s <= 256
-                assert s == mla.choose_num_splits(batch, L, kd)
+                assert s == mla.choose_num_splits(batch, L, kd, q_dtype=qd)
                 assert s == 1 or (L + s - 1) // s >= 32  # no split shorter than one sub-tile
     # a full wave of requests needs no split; small batches split
     assert mla.choose_num_splits(256, 8192, mla.FP8) == 1
     assert mla.choose_num_splits(4, 8192, mla.FP8) >= 16
     assert mla.choose_num_splits(32, 1024, mla.FP8) >= 4
+    # unknown format codes fall back to bf16 Q / fp8 cache
+    assert mla.choose_num_splits(32, 1024, 99, q_dtype=77) == mla.choose_num_splits(32, 1024, mla.FP8)
 
 
-def split_table():
-    path = os.path.join(os.path.dirname(os.path.dirname(__file__)), "mla_latent_kv_13_amd", "csrc", "split_table.inc")
+TABLE_ROW = re.compile(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), ([0-9.]+), (\d+), (\d+), ([0-9.]+)\}")
+
+
+def tune_table(path=None):
+    path = path or os.path.join(os.path.dirname(os.path.dirname(__file__)), "mla_latent_kv_13_amd", "csrc",
+                                "tune_table.inc")
     rows = []
     for line in open(path):
-        m = re.match(r"\{(\d+), (\d+), (\d+), (\d+), ([0-9.]+), (\d+), ([0-9.]+)\}", line.strip())
+        m = TABLE_ROW.match(line.strip())
         if m:
             g = m.groups()
-            rows.append((int(g[0]), int(g[1]), int(g[2]), int(g[3]), float(g[4]), int(g[5]), float(g[6])))
+            rows.append(tuple(float(x) if "." in x else int(x) for x in g))
     return rows
 
 
-def test_split_table_is_used_and_matched_by_the_model(lib):
-    rows = split_table()
-    assert len(rows) == 24  # 4 batches x 2 lengths x 3 cache formats
-    agree = 0
-    for batch, kv_len, kd, s, us, model_s, model_us in rows:
-        assert mla.choose_num_splits(batch, kv_len, kd) == s
-        # the cost model alone (another CU count bypasses the MI355X table)
-        # is the pick the table records for it, and that pick measured within
-        # 6 % of the tuned optimum (near-ties may fall either way)
-        assert mla.choose_num_splits(batch, kv_len, kd, 257) == model_s, (batch, kv_len, kd)
-        assert model_us <= 1.06 * us, (batch, kv_len, kd, model_s, model_us, s, us)
-        agree += model_s == s
-    assert agree >= 22
+def test_tuned_table_drives_both_heuristics(lib):
+    """Every grid shape and format pair has a measured row; on 256 CUs both
+    heuristics return its fastest (split count, page size); one CU more
+    bypasses the table and returns the cost models' own picks, which the row
+    records with their measured time."""
+    rows = tune_table()
+    assert len(rows) == 40  # 4 batches x 2 lengths x 5 format pairs
+    assert len({r[:4] for r in rows}) == 40
+    near = 0
+    for batch, kv_len, qd, kd, s, p, us, ms, mp, mus in rows:
+        assert mla.choose_num_splits(batch, kv_len, kd, q_dtype=qd) == s
+        assert mla.recommend_page_size(batch, kv_len, qd, kd) == p
+        assert mla.choose_num_splits(batch, kv_len, kd, 257, q_dtype=qd) == ms, (batch, kv_len, qd, kd)
+        assert mla.recommend_page_size(batch, kv_len, qd, kd, 257) == mp, (batch, kv_len, qd, kd)
+        assert mus >= us
+        near += mus <= 1.10 * us
+    # the fallback models land within 10 % of the measured optimum on most of the grid
+    assert near >= 32, near
 
 
-def test_split_table_rebuild_from_log(lib, tmp_path):
+def test_tune_table_rebuild_from_log(lib, tmp_path):
     """The tuner's offline path: a sweep log becomes a table whose rows hold
-    the fastest split count and the cost model's own pick with its time."""
-    from mla_latent_kv_13_amd import tune_splits as ts
+    the fastest (S, P) and the cost models' pick with its time."""
+    from mla_latent_kv_13_amd import tune as tn
 
     log = tmp_path / "sweep.jsonl"
     with open(log, "w") as f:
         f.write("not json: a warning line the tuner skips\n")
-        for batch in ts.BATCHES:
-            for kv_len in ts.KV_LENS:
-                for fmt, code in ts.FORMATS:
-                    model = ts.model_splits(batch, kv_len, code)
-                    for s in sorted(set(ts.SPLITS) | {model}):
-                        # a synthetic timing with its minimum at S = 2
-                        us = 10.0 + abs(s - 2)
-                        f.write(f'{{"batch": {batch}, "kv_len": {kv_len}, "kv": "{fmt}", "splits": {s}, "us": {us}}}\n')
+        f.write('{"kernel_source_sha256": "ab12cd34ef56ab78cd90ef12ab34cd56"}\n')
+        for batch in tn.BATCHES:
+            for kv_len in tn.KV_LENS:
+                for q, kv in tn.PAIRS:
+                    ms, mp = tn.model_pick(batch, kv_len, q, kv)
+                    pts = {(s, 8) for s in tn.SPLITS} | {(2, p) for p in tn.PAGES} | {(ms, mp)}
+                    for s, p in sorted(pts):
+                        # a synthetic timing with its minimum at S = 2, P = 4
+                        us = 10.0 + abs(s - 2) + abs(p - 4) / 8
+                        f.write(f'{{"batch": {batch}, "kv_len": {kv_len}, "q": "{q}", "kv": "{kv}", '
+                                f'"splits": {s}, "page": {p}, "us": {us}}}\n')
     out = tmp_path / "table.inc"
-    rows = ts.from_log(str(log), str(out))
-    assert len(rows) == 24
+    rows = tn.from_log(str(log), str(out))
+    assert len(rows) == 40
     text = open(out).read()
-    parsed = [tuple(float(x) for x in m.groups())
-              for m in re.finditer(r"\{(\d+), (\d+), (\d+), (\d+), ([0-9.]+), (\d+), ([0-9.]+)\}", text)]
-    assert len(parsed) == 24
-    for (batch, kv_len, code, s, us, model_s, model_us), row in zip(parsed, rows):
-        assert (int(batch), int(kv_len), int(code)) == row[:3]
-        assert int(s) == 2 and us == 10.0
-        assert int(model_s) == ts.model_splits(int(batch), int(kv_len), int(code))
-        assert model_us == 10.0 + abs(model_s - 2)
+    assert "ab12cd34ef56ab78" in text  # the kernel the sweep was taken on
+    parsed = tune_table(str(out))
+    assert len(parsed) == 40
+    for row, r in zip(parsed, rows):
+        batch, kv_len, qd, kd, s, p, us, ms, mp, mus = row
+        assert (batch, kv_len, qd, kd) == r[:4]
+        assert (s, p, us) == (2, 4, 10.0)
+        q = {0: "bf16", 1: "fp8", 2: "mxfp4"}[qd]
+        kv = {0: "bf16", 1: "fp8", 2: "mxfp4"}[kd]
+        assert (ms, mp) == tn.model_pick(batch, kv_len, q, kv)
+        assert mus == 10.0 + abs(ms - 2) + abs(mp - 4) / 8
 
 
 def test_stream_read_argument_errors(lib):
@@ -175,8 +193,22 @@ def test_stream_read_argument_errors(lib):
 
 
 def test_page_size_recommendation(lib):
-    assert mla.recommend_page_size(4, 1024) >= 1
-    assert mla.recommend_page_size(256, 8192) >= 1
+    """Off the grid (or on another CU count) the model: a power of two up to
+    16, at most a quarter of the request, never shrinking as requests grow."""
+    for qd, kd in ((mla.BF16, mla.FP8), (mla.MXFP4, mla.MXFP4), (mla.BF16, mla.MIXED)):
+        for batch in (1, 3, 100, 256, 5000):
+            prev = 0
+            for L in (1, 2, 3, 5, 8, 17, 40, 64, 100, 500, 1024, 3000, 8192, 10 ** 6):
+                p = mla.recommend_page_size(batch, L, qd, kd, 257)
+                assert p in (1, 2, 4, 8, 16)
+                assert p == 1 or 4 * p <= L
+                assert p >= prev
+                prev = p
+            assert prev == 16
+    assert mla.recommend_page_size(0, 8192) == 1 and mla.recommend_page_size(4, 0) == 1
+    # on the grid the table answers for each format pair
+    for batch, kv_len, qd, kd, s, p, *_ in tune_table():
+        assert mla.recommend_page_size(batch, kv_len, qd, kd) == p
 
 
 def test_product_path_does_not_touch_the_oracle():
