@@ -38,9 +38,39 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "bs256_kv8192_a16w8"
 FMT = {"bf16": mla.BF16, "fp8": mla.FP8, "mxfp4": mla.MXFP4}
 FLOPS_PER_TOKEN = 2 * 16 * (576 + 512)  # QK^T and P*V multiply-adds, all 16 heads
-PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense
+# MI355X dense MFMA peaks (AMD's published figures without sparsity), TFLOP/s
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 KERNEL_SOURCE = os.path.join(REPO, "mla_latent_kv_13_amd", "csrc", "mla_decode.hip")
-TRAFFIC_FILE = os.path.join(REPO, "profiles", "stage1_a16w8_bs256_kv8192_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(REPO, "profiles", "stage1_hbm_traffic_per_workload.txt")
+
+
+def mfma_tiles(q_fmt: str, kv_fmt: str):
+    """MFMA operand type of the QK^T and P*V tiles, and the multiply-adds each
+    executes per token and head (the reduction padded to the instruction's
+    K; two passes where bf16 Q runs as an exact fp8 hi + lo pair)."""
+    if q_fmt == "bf16" and kv_fmt in ("bf16", "fp8"):
+        qk, qk_k = "bf16", 576  # an fp8 cache is widened exactly to bf16 for 16x16x32 bf16
+    elif kv_fmt == "fp8":
+        qk, qk_k = "fp8", 640  # 16x16x128 f8f6f4, five K blocks
+    elif q_fmt == "mxfp4":
+        qk, qk_k = "fp4", 640
+    else:
+        qk, qk_k = "fp8", 2 * 640  # e2m1 K x fp8 hi and lo: fp4 x fp8 runs at the fp8 rate
+    return {"qk": (qk, qk_k), "pv": ("bf16", 512)}
+
+
+def mfma_report(q_fmt, kv_fmt, tokens, us):
+    """Achieved MFMA rate of each tile against the dense peak of its own
+    operand type: algorithmic multiply-adds (576 / 512 per token and head) and
+    executed ones (padded, two passes for the hi + lo pair)."""
+    out = {}
+    for tile, (dt, k_exec) in mfma_tiles(q_fmt, kv_fmt).items():
+        k_alg = 576 if tile == "qk" else 512
+        alg = 2.0 * 16 * tokens * k_alg / (us * 1e-6) / 1e12
+        exe = 2.0 * 16 * tokens * k_exec / (us * 1e-6) / 1e12
+        out[tile] = {"dtype": dt, "algorithmic_tflops": round(alg, 2), "executed_tflops": round(exe, 2),
+                     "peak_tflops": PEAK_MFMA_TFLOPS[dt], "frac": round(exe / PEAK_MFMA_TFLOPS[dt], 4)}
+    return out
 
 
 def kernel_source_sha256() -> str:
@@ -49,24 +79,32 @@ def kernel_source_sha256() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per stage-1 launch from the committed FETCH_SIZE/WRITE_SIZE summary.
+    """HBM bytes per stage-1 launch of `workload` from the committed FETCH_SIZE /
+    WRITE_SIZE summary (each counter scaled by what it reads for the library's
+    own streaming-read kernel over a known byte count).
 
-    Only reported for the workload the counters were taken on, and only while
-    the kernel source is byte-identical to the one they were taken from (the
-    summary records its sha256); otherwise None.
+    Reported only while the kernel source is byte-identical to the one the
+    counters were taken on (the summary records its sha256); otherwise None.
     """
-    if workload != HEADLINE or not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    fields = {}
+    sha, rows = None, {}
     with open(TRAFFIC_FILE) as f:
         for line in f:
             k, sep, v = line.strip().partition(":")
-            if sep and v.split():
-                fields[k.strip()] = v.split()[0]
-    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+            if not sep:
+                continue
+            if k.strip() == "kernel_source_sha256" and v.split():
+                sha = v.split()[0]
+            elif k.startswith("workload "):
+                fields = dict(zip(v.split()[::2], v.split()[1::2]))
+                rows[k.split()[1]] = fields
+    if sha != kernel_source_sha256() or workload not in rows:
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        r = rows[workload]
+        return {"fetch_bytes": int(r["fetch_bytes"]), "write_bytes": int(r["write_bytes"]),
+                "traffic_bytes": int(r["traffic_bytes"])}
     except (KeyError, ValueError):
         return None
 
@@ -125,15 +163,15 @@ def time_calls(call, steps, warmup, warmup_s, per_graph=None):
     graph replays are timed with HIP events on the launch stream: without
     `per_graph`, exactly `steps` calls in up to five equal groups; with it
     (rotated replicas), five groups of whole graphs covering at least `steps`.
-    Returns (median, min, max) ms per call over the groups, the host wall time
-    per call and the number of timed calls."""
+    Returns (median, min, max, p90) ms per call over the groups, the host wall
+    time per call and the number of timed calls."""
     if per_graph is None:
-        # exactly `steps` timed calls: up to five equal groups of one graph each
+        # exactly `steps` timed calls: up to ten equal groups of one graph each
         steps = max(1, steps)
-        ngroups = next(g for g in (5, 4, 3, 2, 1) if steps % g == 0)
+        ngroups = next(g for g in (10, 5, 4, 3, 2, 1) if steps % g == 0)
         per_graph = steps // ngroups
     else:
-        ngroups = 5
+        ngroups = 10
     reps_per_group = max(1, math.ceil(steps / (ngroups * per_graph)))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -166,7 +204,8 @@ def time_calls(call, steps, warmup, warmup_s, per_graph=None):
     wall = (time.perf_counter() - t0) / calls
     group_ms = sorted(e0.elapsed_time(e1) / (reps_per_group * per_graph) for e0, e1 in evs)
     del graph
-    return group_ms[len(group_ms) // 2], group_ms[0], group_ms[-1], wall, calls
+    p90 = group_ms[min(len(group_ms) - 1, math.ceil(0.9 * len(group_ms)) - 1)]
+    return group_ms[len(group_ms) // 2], group_ms[0], group_ms[-1], p90, wall, calls
 
 
 def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
@@ -174,8 +213,8 @@ def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
     (the headline figure).  With `extras`, also time it on one set of buffers
     (warm, Infinity-Cache resident when small) and with the library heuristic's
     split count when that differs."""
-    S = w.num_splits or mla.choose_num_splits(w.batch, w.kv_len, FMT[w.kv_fmt])
-    S_heur = mla.choose_num_splits(w.batch, w.kv_len, FMT[w.kv_fmt])
+    S_heur = mla.choose_num_splits(w.batch, w.kv_len, FMT[w.kv_fmt], q_dtype=FMT[w.q_fmt])
+    S = w.num_splits or S_heur
     ops = build_inputs(w, device)
     ws_bytes = max(mla.workspace_bytes(w.batch, S), mla.workspace_bytes(w.batch, S_heur))
     work = sum(v.numel() * v.element_size() for v in ops.values() if v is not None) + ws_bytes + w.batch * 16 * 1024
@@ -193,17 +232,19 @@ def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
         return call
 
     per_graph = nrep if nrep > 1 else None
-    ev_ms, mn, mx, wall, calls = time_calls(caller(S, nrep), steps, warmup, warmup_s, per_graph)
+    ev_ms, mn, mx, p90, wall, calls = time_calls(caller(S, nrep), steps, warmup, warmup_s, per_graph)
     nbytes = compulsory_bytes(w, w.page_size)
     res = {
         "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q": w.q_fmt, "kv": w.kv_fmt,
         "page_size": w.page_size, "num_splits": S, "replicas": nrep, "timed_calls": calls,
         "us_per_call": round(ev_ms * 1e3, 3), "us_min": round(mn * 1e3, 3),
-        "us_max": round(mx * 1e3, 3), "wall_us_per_call": round(wall * 1e6, 3),
+        "us_p90": round(p90 * 1e3, 3), "us_max": round(mx * 1e3, 3), "wall_us_per_call": round(wall * 1e6, 3),
         "compulsory_bytes": nbytes, "gbs": round(nbytes / (ev_ms * 1e-3) / 1e9, 1),
         "frac_of_peak": round(nbytes / (ev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "partial_bytes": 2 * mla.workspace_bytes(w.batch, S),
         "tflops": round(FLOPS_PER_TOKEN * w.batch * w.kv_len / (ev_ms * 1e-3) / 1e12, 2),
+        "mfma": mfma_report(w.q_fmt, w.kv_fmt, w.batch * w.kv_len, ev_ms * 1e3),
+        "traffic": measured_traffic(w.name),
     }
     if extras and w.q_fmt != "bf16":
         # end to end from bf16 Q: the Q quantiser (one launch) plus the decode
@@ -341,48 +382,71 @@ def read_ceiling(nbytes, device, steps=50):
     return round(nbytes / (ms * 1e-3) / 1e9, 1), round(ms * 1e3, 3)
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of the headline workload (whole requests, all heads)."""
+def cpu_oracle_call(w, device="cuda"):
+    """One full call of the fp64 oracle for workload `w` on the host cores.
+
+    The inputs are the workload's own (same seeds, generated on the device as
+    for the GPU run, then copied to the host) and are quantised outside the
+    timed region: mxfp4 by the oracle's quantiser, fp8 by torch's CPU cast of
+    clamp(x / scale) with the oracle's scale (the oracle's own exhaustive
+    fp8 search gives the same codes, as its tests pin against that cast, but
+    would take minutes on a 1.2 G-element cache).  The timed region is one
+    oracle decode of every (request, head) pair over the shuffled paged cache,
+    with one OpenMP thread per core this process may run on."""
     import numpy as np
 
     import oracle
 
     cores = len(os.sched_getaffinity(0))
-    case = synth.workload_case(w, device="cuda")
+    case = synth.workload_case(w, device=device)
     kv_bits = case["kv"].view(torch.int16).cpu().numpy().view(np.uint16)
     q_bits = case["q"].view(torch.int16).cpu().numpy().view(np.uint16)
+    ind = case["kv_indptr"].cpu().numpy()
+    pt = case["page_table"].cpu().numpy()
     del case
-    sc = oracle.fp8_scale_from_amax(oracle.amax_bf16(kv_bits)) if w.kv_fmt == "fp8" else None
-    P = w.page_size
-    npages = math.ceil(w.batch * w.kv_len / P)
-    perm = (torch.randperm(npages, generator=torch.Generator().manual_seed(synth.BASE_SEED + w.index + 1000)).numpy()
-            if w.shuffle else np.arange(npages))
+    def fp8_codes(bits, scale):
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float()
+        c = torch.clamp(x / scale, -448.0, 448.0).to(torch.float8_e4m3fn)
+        return c.view(torch.uint8).numpy()
 
-    def run(n):
-        # the first n requests, compacted to their own rows behind an identity page table
-        gpos = np.arange(n * w.kv_len)
-        rows = perm[gpos // P].astype(np.int64) * P + gpos % P
-        sub = np.ascontiguousarray(kv_bits[rows])
-        if w.kv_fmt == "fp8":
-            kv, _ = oracle.quant_fp8(sub, sc)
-            extra = {"kv_dtype": "fp8", "kv_scale": sc}
-        else:
-            kv, extra = sub, {"kv_dtype": "bf16"}
-        ind = (np.arange(n + 1) * w.kv_len).astype(np.int32)
-        t0 = time.perf_counter()
-        oracle.decode(q_bits[:n], kv, ind, np.arange(n * w.kv_len, dtype=np.int32), 1, nthreads=cores, **extra)
-        return time.perf_counter() - t0
+    t0 = time.perf_counter()
+    args = {}
+    if w.kv_fmt == "fp8":
+        sc = oracle.fp8_scale_from_amax(oracle.amax_bf16(kv_bits))
+        kv = fp8_codes(kv_bits, sc)
+        args.update(kv_dtype="fp8", kv_scale=sc)
+    elif w.kv_fmt == "mxfp4":
+        kv, e8 = oracle.quant_mxfp4(kv_bits)
+        args.update(kv_dtype="mxfp4", kv_e8m0=e8)
+    else:
+        kv = kv_bits
+    del kv_bits
+    if w.q_fmt == "fp8":
+        qs = float(np.float32(w.q_scale))
+        q = fp8_codes(q_bits, qs)
+        args.update(q_dtype="fp8", q_scale=qs)
+    elif w.q_fmt == "mxfp4":
+        qp, qe = oracle.quant_mxfp4(q_bits.reshape(w.batch * 16, 576))
+        q = qp.reshape(w.batch, 16, 288)
+        args.update(q_dtype="mxfp4", q_e8m0=qe)
+    else:
+        q = q_bits
+    t_quant = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.decode(q, kv, ind, pt, w.page_size, nthreads=cores, **args)
+    t = time.perf_counter() - t0
+    return {"s_per_call": round(t, 3), "cores": cores, "quantise_s_untimed": round(t_quant, 2),
+            "sample": f"one full call: {w.batch} requests x 16 heads x {w.kv_len} tokens"}
 
-    t1 = run(1)
-    n = max(1, min(w.batch, int(budget_s / max(t1, 1e-3))))
-    t = run(n) if n > 1 else t1
-    per_req = t / n
-    full = per_req * w.batch
-    nbytes = compulsory_bytes(w, P)
-    return {"value": round(nbytes / full / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {w.batch} requests x 16 heads x {w.kv_len} tokens ({w.name}), fp64 C oracle, "
-                      f"{t:.1f} s; full call extrapolated to {full:.1f} s",
-            "us_per_call": round(full * 1e6, 1)}
+
+def cpu_baseline(w, oracle_call):
+    """The headline's CPU baseline object from its full oracle call."""
+    nbytes = compulsory_bytes(w, w.page_size)
+    t = oracle_call["s_per_call"]
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": oracle_call["cores"], "kind": "oracle",
+            "sample": f"{oracle_call['sample']} ({w.name}), fp64 C oracle with OpenMP, measured (no extrapolation); "
+                      f"its own quantisation of the inputs ({oracle_call['quantise_s_untimed']} s) is untimed",
+            "us_per_call": round(t * 1e6, 1)}
 
 
 def main():
@@ -397,9 +461,10 @@ def main():
                     help="time only this extra workload (for profiling) and print its JSON")
     ap.add_argument("--warmup-seconds", type=float, default=0.3,
                     help="minimum warm-up time per workload (0 for short profiled runs)")
-    ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="instead of decoding, run a plain device-to-device copy of this many bytes "
-                         "(the known-size reference used to scale HBM byte counters)")
+    ap.add_argument("--calib-bytes", type=int, default=0,
+                    help="instead of decoding, read this many bytes with the library's streaming-read kernel "
+                         "and write as many with a fill kernel (the known-size references that scale the "
+                         "FETCH_SIZE and WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode path has no multi-GPU mode "
@@ -410,19 +475,17 @@ def main():
         sys.exit(2)
     mla.load()
     device = "cuda"
-    if args.copy_bytes:
-        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=device)
+    if args.calib_bytes:
+        n = args.calib_bytes // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.float32, device=device)
         dst = torch.empty_like(src)
-        for _ in range(args.warmup):
-            dst.copy_(src)
+        sink = torch.zeros(1, dtype=torch.int32, device=device)
+        for _ in range(args.warmup + args.steps):
+            mla.stream_read(src, sink)  # reads n bytes, writes none
+            dst.fill_(2.0)              # writes n bytes, reads none
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / args.steps
-        print(json.dumps({"metric": "device copy", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
-                          "us_per_copy": round(dt * 1e6, 2), "gbs": round(2 * src.numel() * 4 / dt / 1e9, 1)}))
+        print(json.dumps({"metric": "counter calibration", "stream_read_bytes": n, "fill_bytes": n,
+                          "launches_each": args.warmup + args.steps}))
         return
     if args.extra_only:
         fn = {"ragged": time_ragged, "multi_token": time_multi_token, "mixed": time_mixed}[args.extra_only]
@@ -448,8 +511,16 @@ def main():
         others.append(time_mixed(max(10, args.steps // 2), args.warmup, device, args.warmup_seconds))
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w)
+        # after every GPU timing, so host work cannot disturb them: one full
+        # oracle call per synthetic workload
+        for entry in [head] + others:
+            ow = synth.WORKLOADS.get(entry["workload"])
+            if ow is None:
+                continue
+            print(f"[bench] cpu oracle, full call: {ow.name}", file=sys.stderr, flush=True)
+            entry["cpu_oracle"] = cpu_oracle_call(ow)
+            entry["gpu_speedup_vs_cpu_oracle"] = round(entry["cpu_oracle"]["s_per_call"] * 1e6 / entry["us_per_call"])
+        cpu = cpu_baseline(w, head["cpu_oracle"])
     gbs = head["gbs"]
     line = {
         "metric": "us/call and achieved HBM GB/s (% of peak) for MLA decode, bs x kv_len",
@@ -470,13 +541,13 @@ def main():
                    "page_size": w.page_size, "num_splits": head["num_splits"], "parallelism": "single GPU"},
         "roofline": {"kernel": "stage1_kernel" + ("" if head["num_splits"] == 1 else " + stage2_kernel"),
                      "bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": head["frac_of_peak"], "traffic": measured_traffic(w.name),
+                     "frac": head["frac_of_peak"],
+                     "traffic": (head["traffic"] or {}).get("traffic_bytes"),
                      "traffic_unit": "bytes per launch",
                      "read_ceiling": {"achieved": ceil_gbs, "us": ceil_us, "bytes": head["compulsory_bytes"],
                                       "kernel": "stream_read_kernel (16-B non-temporal loads, read once)"},
                      "frac_of_read_ceiling": round(head["gbs"] / ceil_gbs, 4)},
-        "mfma": {"dtype": "bf16" if w.kv_fmt != "mxfp4" else "bf16/fp4", "achieved_tflops": head["tflops"],
-                 "peak_tflops": PEAK_MFMA_BF16_TFLOPS, "frac": round(head["tflops"] / PEAK_MFMA_BF16_TFLOPS, 4)},
+        "mfma": head["mfma"],
         "cpu_baseline": cpu,
         "workloads": [head] + others,
     }
