@@ -116,6 +116,29 @@ int mla_decode(const void* q, int32_t q_dtype, const void* q_scale,
                void* stream);
 
 /*
+ * mla_decode_noalloc - mla_decode with no workspace argument, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The split partials live in a
+ * static device array of MLA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends; its address is looked up on
+ * the first call on a device.  The call allocates nothing and calls no
+ * allocating routine.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap on one GPU (different streams, or concurrent host threads
+ * enqueueing before the previous call has run) race on it and must be
+ * serialised by the caller; no part of it needs to start at zero (each call
+ * writes every partial it reads).  Arguments, output and errors as for
+ * mla_decode, plus MLA_ERR_WORKSPACE when mla_workspace_bytes(batch,
+ * num_splits) exceeds MLA_NOALLOC_SCRATCH_BYTES (e.g. batch 256 at 4 splits)
+ * and MLA_ERR_DEVICE when the array's device address cannot be looked up.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mla_decode_noalloc(const void* q, int32_t q_dtype, const void* q_scale,
+                       const void* kv_cache, int32_t kv_dtype, const void* kv_scale, int64_t num_kv_rows,
+                       const int32_t* kv_indptr, int32_t batch,
+                       const int32_t* page_table, const int32_t* page_indptr, int32_t page_size,
+                       int32_t num_splits, void* out, void* stream);
+
+/*
  * mla_validate - the host-side argument checks of mla_decode, with the same
  * arguments, returning the status mla_decode would return before launching.
  * Makes no HIP call and touches no device memory (usable without a GPU).

@@ -29,7 +29,8 @@ __all__ = [
     "BF16", "FP8", "MXFP4", "HEADS", "D_QK", "D_V",
     "load", "decode", "workspace_bytes", "choose_num_splits", "recommend_page_size",
     "quantize_fp8", "quantize_mxfp4", "validate", "status_string", "StatusError",
-    "mxfp4_scale_buffer", "MIXED", "decode_mixed", "validate_mixed", "new_workspace",
+    "mxfp4_scale_buffer", "MIXED", "decode_mixed", "validate_mixed", "new_workspace", "decode_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 BF16, FP8, MXFP4 = 0, 1, 2
@@ -49,7 +50,7 @@ EXPORTS = ("mla_decode", "mla_validate", "mla_workspace_bytes", "mla_choose_num_
            "mla_recommend_page_size", "mla_quantize_fp8", "mla_quantize_mxfp4", "mla_stream_read",
            "mla_plan_worklist", "mla_worklist_workspace_bytes", "mla_decode_worklist", "mla_decode_rows",
            "mla_workspace_bytes_rows", "mla_decode_mixed", "mla_validate_mixed", "mla_check_tables",
-           "mla_status_string", "mla_abi_version")
+           "mla_decode_noalloc", "mla_status_string", "mla_abi_version")
 
 
 class StatusError(RuntimeError):
@@ -72,6 +73,8 @@ def load():
             L.mla_decode.argtypes = _DECODE_ARGS + [_c_void]
             L.mla_validate.restype = ctypes.c_int
             L.mla_validate.argtypes = _DECODE_ARGS
+            L.mla_decode_noalloc.restype = ctypes.c_int
+            L.mla_decode_noalloc.argtypes = _DECODE_ARGS[:14] + [_c_void]
             L.mla_workspace_bytes.restype = _c_size
             L.mla_workspace_bytes.argtypes = [_c_int32, _c_int32]
             L.mla_choose_num_splits.restype = _c_int32
@@ -237,6 +240,33 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
         rc = L.mla_decode_rows(*args[:3], rows, *args[3:], _stream(stream))
     if rc:
         raise StatusError("mla_decode" if rows == HEADS else "mla_decode_rows", rc)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Tensor,
+                   page_size: int, num_splits: int, out: torch.Tensor, *, q_scale=None, kv_scale=None,
+                   page_indptr=None, stream=None):
+    """mla_decode_noalloc: single-token decode into a caller-allocated `out`
+    [batch,16,512] bf16 with the split partials in the library's static
+    per-GPU scratch (workspace_bytes(batch, num_splits) must not exceed
+    NOALLOC_SCRATCH_BYTES).  Nothing is allocated; calls that overlap on one
+    GPU race on the scratch."""
+    batch = kv_indptr.numel() - 1
+    rows = _q_rows(q, batch)
+    if rows != HEADS:
+        raise ValueError("decode_noalloc takes 16 query rows per request")
+    if out is None:
+        raise ValueError("decode_noalloc writes into a caller-allocated out")
+    _check_operands(q, kv_cache, kv_scale, out, batch, rows)
+    _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out)
+    args = _decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale, kv_scale, page_indptr,
+                        out, None)
+    rc = (_lib or load()).mla_decode_noalloc(*args[:14], _stream(stream))
+    if rc:
+        raise StatusError("mla_decode_noalloc", rc)
     return out
 
 

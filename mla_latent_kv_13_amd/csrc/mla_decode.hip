@@ -39,6 +39,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cstdint>
 #include <type_traits>
 #include <utility>
@@ -1534,6 +1535,30 @@ int device_cus() {
   return n;
 }
 
+// Scratch of mla_decode_noalloc: the split partials in a file-scope device
+// array (each GPU the library runs on holds its own copy until the process
+// ends), for callers that cannot allocate.  Host code never uses the array's
+// name as an address: its device address is looked up once per device.
+__device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+void* scratch_ptr() {
+  static std::atomic<void*> ptrs[64];
+  static std::mutex init;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(init);
+  p = ptrs[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    ptrs[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
 int grid_for(int64_t n, int per) {
   int64_t g = (n + per - 1) / per;
   if (g < 1) g = 1;
@@ -1660,6 +1685,25 @@ int mla_decode(const void* q, int32_t q_dtype, const void* q_scale, const void* 
   return decode_launch(q, q_dtype, q_scale, kHeads, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch,
                        page_table, page_indptr, page_size, num_splits, nullptr, 0, nullptr, 0, out, workspace,
                        workspace_bytes, stream);
+}
+
+int mla_decode_noalloc(const void* q, int32_t q_dtype, const void* q_scale, const void* kv_cache, int32_t kv_dtype,
+                       const void* kv_scale, int64_t num_kv_rows, const int32_t* kv_indptr, int32_t batch,
+                       const int32_t* page_table, const int32_t* page_indptr, int32_t page_size, int32_t num_splits,
+                       void* out, void* stream) {
+  const size_t need = mla_workspace_bytes(batch, num_splits);
+  if (need > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need) {
+    ws = scratch_ptr();
+    if (!ws) return MLA_ERR_DEVICE;
+  }
+  const int rc = mla_validate(q, q_dtype, q_scale, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch,
+                              page_table, page_indptr, page_size, num_splits, out, ws, need ? MLA_NOALLOC_SCRATCH_BYTES : 0);
+  if (rc != MLA_OK || batch == 0) return rc;
+  return decode_launch(q, q_dtype, q_scale, kHeads, kv_cache, kv_dtype, kv_scale, num_kv_rows, kv_indptr, batch,
+                       page_table, page_indptr, page_size, num_splits, nullptr, 0, nullptr, 0, out, ws,
+                       need ? MLA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int mla_decode_rows(const void* q, int32_t q_dtype, const void* q_scale, int32_t q_rows, const void* kv_cache,
