@@ -856,3 +856,91 @@ def test_long_request(orc, S):
     ref, _ = oracle_decode(case, o, orc, pairs=pairs)
     for b, h in pairs:
         check_close(out[b, h], ref[b, h], what=f"long request S={S} b={b} h={h}", l2=1e-2)
+
+
+# ------------------------------------------ every output of the full-size shapes
+def _fp8_codes_cpu(bits_u16, scale):
+    """e4m3fn codes of clamp(x / scale) by torch's CPU cast: the oracle's own
+    quantiser gives the same codes (its CPU pins compare the two), without its
+    minute-long exhaustive search over a 1.2 G-element cache."""
+    x = torch.from_numpy(bits_u16.view(np.int16)).view(torch.bfloat16).float()
+    return torch.clamp(x / scale, -448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("name", ["bs256_kv8192_a16w8", "bs256_kv8192_mxfp4"])
+def test_full_size_every_output(orc, name):
+    """Every (request, head) output of the headline shape and of the bf16-Q
+    mxfp4 shape, at the stated split count, against one full oracle call on
+    the same quantised cache, element by element: this covers every
+    workgroup index (XCD placement, two-wave workgroups at S = 2) that the
+    sampled checks reach only in part."""
+    w = synth.WORKLOADS[name]
+    print(f"[parity-every] {name}", flush=True)
+    S = w.num_splits or mla.choose_num_splits(w.batch, w.kv_len, FMTS[w.kv_fmt], q_dtype=FMTS[w.q_fmt])
+    case = synth.workload_case(w, device=DEV)
+    kv_bits = bits(case["kv"])
+    o = {"q": bits(case["q"]), "q_dtype": "bf16"}
+    if w.kv_fmt == "fp8":
+        kv_g, ks_g = mla.quantize_fp8(case["kv"])
+        sc = orc.fp8_scale_from_amax(orc.amax_bf16(kv_bits))
+        assert float(ks_g.item()) == sc
+        codes = _fp8_codes_cpu(kv_bits, sc)
+        assert np.array_equal(u8(kv_g), codes)
+        o.update(kv=codes, kv_dtype="fp8", kv_scale=sc)
+    else:
+        kv_g, ks_g = mla.quantize_mxfp4(case["kv"])
+        packed, e8 = orc.quant_mxfp4(kv_bits)
+        assert np.array_equal(u8(kv_g), packed) and np.array_equal(u8(ks_g), e8)
+        o.update(kv=packed, kv_dtype="mxfp4", kv_e8m0=e8)
+    out = mla.decode(case["q"], kv_g, case["kv_indptr"], case["page_table"], w.page_size, S, kv_scale=ks_g)
+    torch.cuda.synchronize()
+    host = {"kv_indptr": case["kv_indptr"].cpu(), "page_table": case["page_table"].cpu(), "page_indptr": None,
+            "page_size": w.page_size}
+    del kv_g, case
+    ref, _ = oracle_decode(host, o, orc)
+    check_close(out, ref, what=f"{name} S={S}, all {w.batch * 16} (request, head) pairs")
+
+
+def test_bf16_q_over_mxfp4_wide_block_range(orc):
+    """bf16 Q over the mxfp4 cache runs QK as an exact fp8 hi + lo pair per
+    32-element block: exact for elements within 2^13 of the block maximum,
+    an absolute resolution of 2^-13 of it below that.  Every Q block here
+    holds one element of 2^5 and others down to 2^-10 (a range of 2^15), or
+    (one request) down to exactly 2^-8 (a range of 2^13); the outputs must
+    meet the contract tolerance against the oracle's exact bf16 Q element by
+    element."""
+    case = synth.make_case(3, [700, 129, 2000], 8, shuffle=True, seed=950)
+    gen = torch.Generator().manual_seed(951)
+    q = case["q"].to(torch.float32).view(3, 16, 18, 32)
+    lead = torch.randint(0, 32, (3, 16, 18), generator=gen)
+    sign = torch.where(torch.rand((3, 16, 18), generator=gen) < 0.5, -1.0, 1.0)
+    q.scatter_(3, lead[..., None], (sign * 32.0)[..., None])
+    # requests 0 and 2: 40 % of each block scaled down to 2^-6 .. 2^-10 (ranges up to 2^15);
+    # request 1: elements of 2^-8 only, a range of exactly 2^13 (the exact limit)
+    tiny = torch.rand((3, 16, 18, 32), generator=gen) < 0.4
+    mag = torch.exp2(-torch.randint(6, 11, (3, 16, 18, 32), generator=gen).to(torch.float32))
+    mag[1] = 2.0 ** -8
+    q = torch.where(tiny & (q.abs() < 32.0), torch.where(q < 0, -1.0, 1.0) * mag, q)
+    q[1] = torch.where(q[1] < 0, -1.0, 1.0) * q[1].abs().clamp(min=2.0 ** -8)
+    case["q"] = q.view(3, 16, 576).to(torch.bfloat16)
+    qb = case["q"].to(torch.float32).view(3, 16, 18, 32).abs()
+    rng = qb.amax(-1) / torch.where(qb > 0, qb, torch.inf).amin(-1)
+    assert float(rng[0].max()) >= 2.0 ** 15 and float(rng[1].max()) == 2.0 ** 13
+    g, o = prepare(case, "bf16", "mxfp4", orc)
+    for S in (1, 3):
+        out = gpu_decode(case, g, S)
+        ref, _ = oracle_decode(case, o, orc)
+        check_close(out, ref, what=f"wide-range bf16 Q over mxfp4, S={S}")
+
+
+@pytest.mark.parametrize("name", [n for n in synth.WORKLOADS])
+def test_full_size_recommended_split_and_page(orc, name):
+    """Each benchmark shape with the page size and split count the tuned
+    heuristic recommends for it (the table's measured optimum), sampled
+    against the oracle."""
+    w = synth.WORKLOADS[name]
+    q, kv = FMTS[w.q_fmt], FMTS[w.kv_fmt]
+    P = mla.recommend_page_size(w.batch, w.kv_len, q, kv)
+    S = mla.choose_num_splits(w.batch, w.kv_len, kv, q_dtype=q)
+    import dataclasses
+    sampled_check(dataclasses.replace(w, page_size=P, shuffle=True), orc, n_req=3, splits=S)
