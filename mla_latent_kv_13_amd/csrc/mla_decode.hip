@@ -337,11 +337,17 @@ __device__ __forceinline__ uint32_t bit_of(uint32_t pm, int t) {
   asm("" : "+v"(b));
   return b;
 }
-// three-input maximum of values that are never NaN (logits and -inf), as one
-// instruction: written out because fmaxf would first quiet each input
+// three- and two-input maxima of values that are never NaN (logits and
+// -inf), as one instruction each: written out because fmaxf would first quiet
+// each input and a select compiles to a compare, a hazard wait and a cndmask
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
 
@@ -349,9 +355,9 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
 // gfx950's cross-row swaps: VALU-only, no LDS round trip.
 __device__ __forceinline__ float group_max(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmax3(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = vmax2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmax3(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  return vmax2(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 __device__ __forceinline__ float group_sum(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -955,12 +961,12 @@ void stage1_kernel(Stage1Args a) {
         if (16 + 4 * g + r >= ntok) sv[4 + r] = -__builtin_huge_valf();
       }
     }
-    float mx = vmax3(vmax3(sv[0], sv[1], sv[2]), vmax3(sv[3], sv[4], sv[5]), fmax3(sv[6], sv[7]));
+    float mx = vmax3(vmax3(sv[0], sv[1], sv[2]), vmax3(sv[3], sv[4], sv[5]), vmax2(sv[6], sv[7]));
     mx = group_max(mx);
 #pragma unroll
     for (int c = 0; c < 32; c += 8) pin_acc8(acc + c);
     if (__any(mx > m_run + kLazy)) {
-      const float m_new = fmax3(m_run, mx);
+      const float m_new = vmax2(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
