@@ -45,3 +45,30 @@ def test_headline_floor_and_target():
     b = bench.compulsory_bytes(synth.WORKLOADS["bs256_kv8192_a16w8"], 8)
     assert round(b / 8e12 * 1e6, 1) == 152.2
     assert round(b / (0.7 * 8e12) * 1e6, 1) == 217.5
+
+
+def test_traffic_summary_is_read_only_for_the_kernel_it_was_taken_on(tmp_path, monkeypatch):
+    """bench.py reports a workload's measured HBM traffic from the committed
+    counter summary only while the kernel source is the one the counters were
+    taken on."""
+    f = tmp_path / "traffic.txt"
+    f.write_text(f"kernel_source_sha256: {bench.kernel_source_sha256()}  (note)\n"
+                 "workload bs64_kv8192_a16w8: fetch_bytes 10 write_bytes 2 traffic_bytes 12\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("bs64_kv8192_a16w8") == {"fetch_bytes": 10, "write_bytes": 2, "traffic_bytes": 12}
+    assert bench.measured_traffic("bs4_kv1024_bf16") is None
+    f.write_text("kernel_source_sha256: " + "0" * 64 + "\n"
+                 "workload bs64_kv8192_a16w8: fetch_bytes 10 write_bytes 2 traffic_bytes 12\n")
+    assert bench.measured_traffic("bs64_kv8192_a16w8") is None
+
+
+def test_mfma_tiles_follow_the_format_pairs():
+    """QK^T runs on bf16 MFMA over bf16 and (widened) fp8 caches with bf16 Q,
+    on fp8 for fp8 Q, on fp4 for mxfp4 Q, and twice on fp8 (hi + lo) for bf16
+    Q over mxfp4; P*V is always bf16 over the 512 value dims."""
+    assert bench.mfma_tiles("bf16", "fp8") == {"qk": ("bf16", 576), "pv": ("bf16", 512)}
+    assert bench.mfma_tiles("fp8", "fp8")["qk"] == ("fp8", 640)
+    assert bench.mfma_tiles("mxfp4", "mxfp4")["qk"] == ("fp4", 640)
+    assert bench.mfma_tiles("bf16", "mxfp4")["qk"] == ("fp8", 1280)
+    r = bench.mfma_report("bf16", "fp8", 2 ** 21, 190.0)
+    assert abs(r["qk"]["algorithmic_tflops"] - 2 * 16 * 2 ** 21 * 576 / 190e-6 / 1e12) < 0.01
