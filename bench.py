@@ -161,8 +161,8 @@ def time_calls(call, steps, warmup, warmup_s, per_graph=None):
     no host launch overhead -- the way a serving loop issues decode.  After a
     warm-up of at least `warmup` calls and `warmup_s` seconds, groups of whole
     graph replays are timed with HIP events on the launch stream: without
-    `per_graph`, exactly `steps` calls in up to five equal groups; with it
-    (rotated replicas), five groups of whole graphs covering at least `steps`.
+    `per_graph`, exactly `steps` calls in up to ten equal groups; with it
+    (rotated replicas), ten groups of whole graphs covering at least `steps`.
     Returns (median, min, max, p90) ms per call over the groups, the host wall
     time per call and the number of timed calls."""
     if per_graph is None:
