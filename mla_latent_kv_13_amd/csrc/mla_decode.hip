@@ -749,7 +749,10 @@ void stage1_kernel(Stage1Args a) {
     for (int X = 0; X < D; ++X) issue_pid(X);
   }
 
-  const float c_log2 = a.sm_scale_log2e * qs * ks;
+  // log2-domain logit scale, kept positive: a zero Q or cache scale then
+  // still gives every valid token the same weight (all logits vanish) and
+  // masked ones none
+  const float c_log2s = fmaxf(a.sm_scale_log2e * qs * ks, 0x1p-126f);
   const float out_mul = KF == FFP8 ? ks : KF == FMIX ? vs : 1.0f;
   // Wait for the page ids and an early Q together, and make the compiler see
   // that Q as complete here, so its own wait for Q cannot drain the
@@ -914,11 +917,14 @@ void stage1_kernel(Stage1Args a) {
         if constexpr (kSplitQ) {
 #pragma unroll
           for (int c = 0; c < 5; ++c) {
+            // hi and lo terms into one chain per token tile: the two chains
+            // alternate, so each 32-cycle MFMA's successor in its chain
+            // issues a full MFMA later
             pin2(u0[c], u1[c]);
             s0 = mfma_fp4_fp8(u0[c], c0[c], q8[c], qhs[c], s0);
             s1 = mfma_fp4_fp8(u1[c], c1[c], q8[c], qhs[c], s1);
-            t0 = mfma_fp4_fp8(u0[c], c0[c], ql[c], qls[c], t0);
-            t1 = mfma_fp4_fp8(u1[c], c1[c], ql[c], qls[c], t1);
+            s0 = mfma_fp4_fp8(u0[c], c0[c], ql[c], qls[c], s0);
+            s1 = mfma_fp4_fp8(u1[c], c1[c], ql[c], qls[c], s1);
           }
         } else {
 #pragma unroll
@@ -938,8 +944,10 @@ void stage1_kernel(Stage1Args a) {
     if constexpr (kSplitDma) {
       if (pend >= 0) issue_part(pend, std::integral_constant<int, KA>(), std::integral_constant<int, KB>());
     }
-    s0 += t0;
-    s1 += t1;
+    if constexpr (!kSplitQ) {  // bf16 Q over mxfp4 K accumulates in one chain per tile
+      s0 += t0;
+      s1 += t1;
+    }
     // the logits are consumed by VALU code: keep them out of the AGPRs that
     // hold the O accumulator
     asm volatile("" : "+v"(s0), "+v"(s1));
@@ -948,11 +956,14 @@ void stage1_kernel(Stage1Args a) {
     // moved when a logit exceeds it by more than 2^kLazy, so the O rescale
     // (all 128 accumulators) runs a handful of times per request; the
     // weights stay <= 2^kLazy and the final division uses the same reference.
+    // raw logits: the log2-domain scale c_log2s > 0 is applied to their
+    // maximum once and to each logit inside its weight's fma (rounding is
+    // monotonic, so the scaled maximum is the maximum of the scaled logits)
     float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = s0[r] * c_log2;
-      sv[4 + r] = s1[r] * c_log2;
+      sv[r] = s0[r];
+      sv[4 + r] = s1[r];
     }
     if (ntok < kSub) {  // wave-uniform: only a range's last sub-tile is short
 #pragma unroll
@@ -962,7 +973,7 @@ void stage1_kernel(Stage1Args a) {
       }
     }
     float mx = vmax3(vmax3(sv[0], sv[1], sv[2]), vmax3(sv[3], sv[4], sv[5]), vmax2(sv[6], sv[7]));
-    mx = group_max(mx);
+    mx = group_max(mx) * c_log2s;
 #pragma unroll
     for (int c = 0; c < 32; c += 8) pin_acc8(acc + c);
     if (__any(mx > m_run + kLazy)) {
@@ -980,8 +991,8 @@ void stage1_kernel(Stage1Args a) {
     const bf16x2_t kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bf16x2_t pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i] - m_run)),
-                           static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i + 1] - m_run))};
+      const bf16x2_t pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c_log2s, -m_run))),
+                           static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c_log2s, -m_run)))};
       // the running sum takes the same bf16-rounded weights the MFMA sees
       psum = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, psum, false);
       pw[i] = bits(pr);
