@@ -1242,7 +1242,7 @@ void stage1_kernel(Stage1Args a) {
 // request yields zeros); a workgroup covers four heads x 512 / kParts columns
 // of one query group.  The LSEs and partial rows of kB splits are loaded
 // together; with kPre the next kB are in flight while a batch is combined,
-// and the running maximum moves with a rescale of the accumulator.  17 to 32
+// and the running maximum moves with a rescale of the accumulator.  9 to 32
 // splits are taken in a single batch of loads (one memory round trip), with
 // four columns per thread so twice as many workgroups share the reads.
 template <int kB, int kC, bool kPre>
