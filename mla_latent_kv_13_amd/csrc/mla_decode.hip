@@ -187,6 +187,22 @@ __device__ __forceinline__ void dma_b32(const void* g, uint32_t m0) {
                : "v"(g), "s"(__builtin_amdgcn_readfirstlane(m0))
                : "memory");
 }
+// Partial results (fp32 O rows and base-2 LSEs) are read back by the
+// combine kernel, on any XCD.  kPol is the store's cache-policy operand:
+// kCpolDev (sc1, device scope) writes them through the L2, so that none are
+// left dirty in it for the write-back at the end of the launch.
+constexpr int kCpolDev = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+template <int kPol>
+__device__ __forceinline__ void st_pol(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, static_cast<int>(off), 0, kPol);
+}
+template <int kPol>
+__device__ __forceinline__ void st_pol(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, kPol);
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -1218,21 +1234,29 @@ void stage1_kernel(Stage1Args a) {
       }
     }
   } else {
-    const size_t prow =
-        ((a.items ? static_cast<size_t>(slot) : static_cast<size_t>(b) * S + s) * G + r) * kHeads + hq;
-    float* po = a.part_o + prow * kDv;
+    // the query group's 16 partial rows (head hq at row prow0 + hq).  A
+    // single round of four-wave workgroups ends all at once, with every
+    // partial still dirty in the L2s: written through, they drain during
+    // the epilogue instead of between the two launches (bs=32 kv=1024 S=8:
+    // 16.8 against 17.8 us per call; 1.5-2.4 % on the other one-round
+    // shapes).  Two-wave workgroups keep write-back stores, which measured
+    // faster there (bs=64 kv=8192 S=8: 62.0 against 63.0 us).
+    constexpr int kCp = kWaves == 4 ? kCpolDev : 0;
+    const size_t prow0 = ((a.items ? static_cast<size_t>(slot) : static_cast<size_t>(b) * S + s) * G + r) * kHeads;
+    const __amdgpu_buffer_rsrc_t po = rsrc_of(a.part_o + prow0 * kDv, kHeads * kDv * 4);
+    const uint32_t ob = static_cast<uint32_t>(hq * kDv * 4);
     if constexpr (KF == FMX) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int h4 = 0; h4 < F / 4; ++h4)
-          *reinterpret_cast<f32x4_t*>(po + 32 * (4 * g + r) + F * w + 4 * h4) =
-              f32x4_t{o[4 * h4][r], o[4 * h4 + 1][r], o[4 * h4 + 2][r], o[4 * h4 + 3][r]} * mul;
+          st_pol<kCp>(po, ob + 4 * (32 * (4 * g + r) + F * w + 4 * h4),
+                      f32x4_t{o[4 * h4][r], o[4 * h4 + 1][r], o[4 * h4 + 2][r], o[4 * h4 + 3][r]} * mul);
     } else {
 #pragma unroll
-      for (int i = 0; i < F; ++i) *reinterpret_cast<f32x4_t*>(po + 16 * (F * w + i) + 4 * g) = o[i] * mul;
+      for (int i = 0; i < F; ++i) st_pol<kCp>(po, ob + 4 * (16 * (F * w + i) + 4 * g), o[i] * mul);
     }
-    if (w == 0 && g == 0) a.part_lse[prow] = lse;
+    if (w == 0 && g == 0) st_pol<kCp>(rsrc_of(a.part_lse + prow0, kHeads * 4), 4 * hq, lse);
   }
 }
 
