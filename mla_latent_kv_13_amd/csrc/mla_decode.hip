@@ -1240,8 +1240,11 @@ void stage1_kernel(Stage1Args a) {
     // the epilogue instead of between the two launches (bs=32 kv=1024 S=8:
     // 16.8 against 17.8 us per call; 1.5-2.4 % on the other one-round
     // shapes).  Two-wave workgroups keep write-back stores, which measured
-    // faster there (bs=64 kv=8192 S=8: 62.0 against 63.0 us).
-    constexpr int kCp = kWaves == 4 ? kCpolDev : 0;
+    // faster there (bs=64 kv=8192 S=8: 62.0 against 63.0 us), and so do the
+    // mxfp4 kernels, whose stores write 16-byte pieces 512 bytes apart: the
+    // L2 must merge those into lines (written through, bs=4 kv=1024 S=8
+    // took 14.4 against 12.4 us with mxfp4 Q).
+    constexpr int kCp = kWaves == 4 && KF != FMX ? kCpolDev : 0;
     const size_t prow0 = ((a.items ? static_cast<size_t>(slot) : static_cast<size_t>(b) * S + s) * G + r) * kHeads;
     const __amdgpu_buffer_rsrc_t po = rsrc_of(a.part_o + prow0 * kDv, kHeads * kDv * 4);
     const uint32_t ob = static_cast<uint32_t>(hq * kDv * 4);
