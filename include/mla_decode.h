@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3  /* 3: q_dtype MLA_Q_BF16_FP8_STATIC */
 
 /* Fixed MLA geometry (page 668813 module constants). */
 #define MLA_NUM_HEADS 16
@@ -59,6 +59,17 @@ extern "C" {
 /* Split cache (mla_decode_mixed): K from an mxfp4 cache, V from an fp8 cache
  * on the same rows.  Accepted as kv_dtype by mla_choose_num_splits only. */
 #define MLA_KV_MXFP4_K_FP8_V 3
+
+/* q_dtype only, with the fp8 cache: Q arrives as bf16 [batch,R,576] and the
+ * stage-1 workgroups quantise it to e4m3fn themselves, code for code as
+ * mla_quantize_fp8 with dynamic == 0 and the static per-tensor scale
+ * *q_scale (device float[1]), before decoding it as fp8 Q.  Page 600081's
+ * fp8 route takes such a static Q scale (`STATIC_Q_ABSMAX`) so that no amax
+ * pass is needed per call; here the quantiser's separate launch goes too.
+ * For every finite Q the output is bit-identical to mla_quantize_fp8
+ * followed by the decode with MLA_DTYPE_FP8_E4M3FN (NaN elements of Q give
+ * unspecified codes there and here). */
+#define MLA_Q_BF16_FP8_STATIC 4
 
 /* Status codes. */
 #define MLA_OK 0
@@ -76,11 +87,14 @@ extern "C" {
 /*
  * mla_decode - split-K MLA decode of `batch` single-token requests.
  *
- * q          [batch,16,576] bf16            (q_dtype = MLA_DTYPE_BF16), or
+ * q          [batch,16,576] bf16            (q_dtype = MLA_DTYPE_BF16 or
+ *                                            MLA_Q_BF16_FP8_STATIC), or
  *            [batch,16,576] e4m3fn bytes    (q_dtype = MLA_DTYPE_FP8_E4M3FN), or
  *            [batch,16,288] packed e2m1     (q_dtype = MLA_DTYPE_MXFP4).
  * q_scale    NULL for bf16; device float[1] per-tensor scale for fp8 (the value
- *            a code is multiplied by); device uint8 e8m0 [batch*16, 18] for mxfp4.
+ *            a code is multiplied by) and for MLA_Q_BF16_FP8_STATIC (the
+ *            static scale Q is quantised with); device uint8 e8m0
+ *            [batch*16, 18] for mxfp4.
  * kv_cache   physical cache rows: [num_kv_rows,576] bf16 | [num_kv_rows,576]
  *            e4m3fn | [num_kv_rows,288] packed e2m1 (byte i: element 2i in the
  *            low nibble, 2i+1 in the high nibble; page 668813's stage-1 kernel).
@@ -104,8 +118,9 @@ extern "C" {
  * workspace  device scratch of at least mla_workspace_bytes(batch, num_splits)
  *            bytes (may be NULL when that is 0); contents on entry are ignored.
  *
- * Supported (q, kv) pairs: (bf16,bf16), (bf16,fp8), (fp8,fp8), (bf16,mxfp4),
- * (mxfp4,mxfp4); anything else returns MLA_ERR_DTYPE.  q, kv_cache, out and
+ * Supported (q, kv) pairs: (bf16,bf16), (bf16,fp8), (fp8,fp8), (bf16 quantised
+ * to fp8 in the call, fp8), (bf16,mxfp4), (mxfp4,mxfp4); anything else
+ * returns MLA_ERR_DTYPE.  q, kv_cache, out and
  * workspace must be 16-byte aligned.
  */
 int mla_decode(const void* q, int32_t q_dtype, const void* q_scale,

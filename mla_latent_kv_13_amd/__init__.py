@@ -30,11 +30,12 @@ __all__ = [
     "load", "decode", "workspace_bytes", "choose_num_splits", "recommend_page_size",
     "quantize_fp8", "quantize_mxfp4", "validate", "status_string", "StatusError",
     "mxfp4_scale_buffer", "MIXED", "decode_mixed", "validate_mixed", "new_workspace", "decode_noalloc",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "Q_BF16_FP8_STATIC",
 ]
 
 BF16, FP8, MXFP4 = 0, 1, 2
 MIXED = 3  # split cache: mxfp4 K + fp8 V (format code for choose_num_splits)
+Q_BF16_FP8_STATIC = 4  # bf16 Q quantised to fp8 inside the decode with a static scale
 HEADS, D_QK, D_V = 16, 576, 512
 MXFP4_ROW_BYTES, MXFP4_ROW_SCALES = 288, 18
 MAX_SPLITS = 256
@@ -193,11 +194,11 @@ def _check_operands(q, kv_cache, kv_scale, out, batch: int, rows: int, what: str
 
 
 def _decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale, kv_scale,
-                 page_indptr, out, workspace):
+                 page_indptr, out, workspace, q_dtype=None):
     batch = kv_indptr.numel() - 1
     num_rows = kv_cache.shape[0] if kv_cache.dim() else 0
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return [_ptr(q), _fmt(q), _ptr(q_scale), _ptr(kv_cache), _fmt(kv_cache), _ptr(kv_scale), num_rows,
+    return [_ptr(q), _fmt(q) if q_dtype is None else int(q_dtype), _ptr(q_scale), _ptr(kv_cache), _fmt(kv_cache), _ptr(kv_scale), num_rows,
             _ptr(kv_indptr), batch, _ptr(page_table), _ptr(page_indptr), int(page_size), int(num_splits),
             _ptr(out), _ptr(workspace), ws_bytes]
 
@@ -211,28 +212,39 @@ def validate(q, kv_cache, kv_indptr, page_table, page_size, num_splits, *, q_sca
 
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Tensor,
            page_size: int, num_splits: int | None = None, *, q_scale=None, kv_scale=None,
-           page_indptr=None, out=None, workspace=None, kv_len_hint: int | None = None, stream=None):
+           page_indptr=None, out=None, workspace=None, kv_len_hint: int | None = None, stream=None,
+           q_fp8_scale=None):
     """MLA decode; returns out [batch,R,512] bf16 (enqueued on the current stream).
 
     q          [B,R,576] bf16 / float8_e4m3fn, or [B,R,288] uint8 (mxfp4, with q_scale e8m0 [B*R,18]);
                R = q_seq_len x heads query rows per request (16 for single-token decode)
     kv_cache   [R,576] bf16 / float8_e4m3fn, or [R,288] uint8 (mxfp4, with kv_scale e8m0 [R,18])
     kv_indptr  int32 [B+1] token offsets; page_table int32 page ids; page_indptr optional int32 [B]
+    q_fp8_scale  with bf16 q over the fp8 cache: a 1-element float32 static scale; the decode then
+               quantises q to fp8 itself, code for code as quantize_fp8(q, q_fp8_scale)
+               (MLA_Q_BF16_FP8_STATIC), in place of a separate quantiser launch
     """
     batch = kv_indptr.numel() - 1
     rows = _q_rows(q, batch)
     _check_operands(q, kv_cache, kv_scale, out, batch, rows)
+    q_dtype = _fmt(q)
+    if q_fp8_scale is not None:
+        if q.dtype != torch.bfloat16 or _fmt(kv_cache) != FP8 or q_scale is not None:
+            raise ValueError("q_fp8_scale takes bf16 q over the fp8 cache, without q_scale")
+        if q_fp8_scale.dtype != torch.float32 or q_fp8_scale.numel() < 1:
+            raise ValueError("q_fp8_scale is a 1-element float32 tensor")
+        q_scale, q_dtype = q_fp8_scale, Q_BF16_FP8_STATIC
     if num_splits is None:
         # one workgroup per 16-row query group: the occupancy is batch x groups
         hint = kv_len_hint if kv_len_hint is not None else max(1, kv_cache.shape[0] // max(batch, 1))
-        num_splits = choose_num_splits(batch * (rows // HEADS), hint, _fmt(kv_cache), q_dtype=_fmt(q))
+        num_splits = choose_num_splits(batch * (rows // HEADS), hint, _fmt(kv_cache), q_dtype=q_dtype)
     if out is None:
         out = torch.empty((batch, rows, D_V), dtype=torch.bfloat16, device=kv_cache.device)
     if workspace is None and batch > 0:
         workspace = new_workspace(workspace_bytes(batch, num_splits, rows), kv_cache.device)
     _dev(q, kv_cache, kv_indptr, page_table, q_scale, kv_scale, page_indptr, out, workspace)
     args = _decode_args(q, kv_cache, kv_indptr, page_table, page_size, num_splits, q_scale, kv_scale, page_indptr,
-                        out, workspace)
+                        out, workspace, q_dtype)
     L = _lib or load()
     if rows == HEADS:
         rc = L.mla_decode(*args, _stream(stream))

@@ -61,6 +61,7 @@ constexpr int FBF16 = MLA_DTYPE_BF16;
 constexpr int FFP8 = MLA_DTYPE_FP8_E4M3FN;
 constexpr int FMX = MLA_DTYPE_MXFP4;
 constexpr int FMIX = MLA_KV_MXFP4_K_FP8_V;  // mxfp4 K + fp8 V, two caches
+constexpr int FQ8S = MLA_Q_BF16_FP8_STATIC;  // bf16 Q, quantised to fp8 in the prologue
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -411,11 +412,55 @@ struct Stage1Args {
 };
 
 // Number of QK MFMA "B operands" (Q fragments) a lane holds, per format pair.
+// The static-scale fp8 quantiser of bf16 Q, on one lane's 32 values of a QK
+// B operand (raw[0..3], eight bf16 each, in dimension order) into their 32
+// e4m3fn codes: each code is the nearest e4m3fn value (ties to even) to the
+// fp32 quotient x / s clamped to +-448, the per-element rule of the fp8
+// quantiser of page 668813 that mla_quantize_fp8 implements.  With
+// r = 1/s correctly rounded, q0 = x r, e = x - q0 s (exact, one fma) and
+// q0 + e r (one fma) is the correctly rounded quotient (Markstein's
+// reciprocal-based division) when nothing overflows or underflows; x is
+// clamped first to +-896 s, beyond which the clamped result is 448 anyway,
+// and the sign is copied from x so that -0 stays -0.  On MI355X the codes
+// matched those of x / s and the software encoder of mla_quantize_fp8 for
+// every finite bf16 x under 4,000 scales spread over [2^-60, 2^60], and the
+// hardware e4m3 encoder matched the software one for every fp32 of
+// magnitude <= 448.  Scales outside that range take the division itself
+// (kExact).
+template <bool kExact>
+__device__ __forceinline__ i32x8_t quant_q_fp8(const u32x4_t raw[4], float s, float r) {
+  const float bnd = 896.0f * s;
+  u32x8_t out;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t u = raw[w >> 1][2 * (w & 1) + (k >> 1)];
+      const float x = __uint_as_float((k & 1) ? (u & 0xffff0000u) : (u << 16));
+      float y;
+      if constexpr (kExact) {
+        y = x / s;
+      } else {
+        const float xc = __builtin_amdgcn_fmed3f(x, -bnd, bnd);
+        const float q0 = xc * r;
+        y = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, xc), r, q0), x);
+      }
+      q[k] = __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f);
+    }
+    i16x2_t p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, q[0], q[1], 1.0f, false);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, q[2], q[3], 1.0f, true);
+    out[w] = __builtin_bit_cast(uint32_t, p);
+  }
+  return __builtin_bit_cast(i32x8_t, out);
+}
+
 template <int QF, int KF> struct QFrag;
 template <> struct QFrag<FBF16, FBF16> { static constexpr int kN = 18; };
 template <> struct QFrag<FBF16, FFP8> { static constexpr int kN = 18; };
 template <> struct QFrag<FBF16, FMX> { static constexpr int kN = 5; };  // hi/lo fp8 pairs
 template <> struct QFrag<FFP8, FFP8> { static constexpr int kN = 5; };
+template <> struct QFrag<FQ8S, FFP8> { static constexpr int kN = 5; };
 template <> struct QFrag<FMX, FMX> { static constexpr int kN = 5; };
 template <> struct QFrag<FBF16, FMIX> { static constexpr int kN = 5; };
 template <> struct QFrag<FMX, FMIX> { static constexpr int kN = 5; };
@@ -441,7 +486,11 @@ void stage1_kernel(Stage1Args a) {
   constexpr int D = L::kD;
   constexpr int NDMA = L::kNdma;
   constexpr int ROW = Kv<KF>::kRow;
-  __shared__ __attribute__((aligned(1024))) char smem[L::kTotal];
+  // bf16 Q quantised in the prologue by four-wave workgroups: each wave
+  // quantises some of the five fp8 B-operand chunks and they meet in LDS
+  // (10 KB past the rings; the 151 KB fp8 layout plus this still fits a CU)
+  constexpr int kQ8Bytes = QF == FQ8S && kWaves == 4 ? 5 * 64 * 32 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[L::kTotal + kQ8Bytes];
   const uint32_t smem0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem));
 
   const int lane = threadIdx.x & 63;
@@ -492,9 +541,13 @@ void stage1_kernel(Stage1Args a) {
   // the fp8 cache, K is widened to bf16 instead (full-rate converts).
   constexpr bool kMxK = KF == FMX || KF == FMIX;  // K from an mxfp4 cache
   constexpr bool kSplitQ = QF == FBF16 && kMxK;
+  // bf16 Q quantised here to fp8 with a static scale: raw bf16 fragments are
+  // held until the loads have landed, then the rest is the fp8-Q kernel
+  constexpr bool kQuantQ = QF == FQ8S;
+  constexpr int QFE = kQuantQ ? FFP8 : QF;  // the Q format the loop computes with
   bf16x8_t qb[QF == FBF16 && !kSplitQ ? NQ : 1];
-  u32x4_t qraw[kSplitQ ? 4 * NQ : 1];
-  i32x8_t q8[QF == FFP8 || kSplitQ ? NQ : 1];
+  u32x4_t qraw[kSplitQ || kQuantQ ? 4 * NQ : 1];
+  i32x8_t q8[QFE == FFP8 || kSplitQ ? NQ : 1];
   i32x8_t ql[kSplitQ ? NQ : 1];
   uint32_t qhs[kSplitQ ? NQ : 1], qls[kSplitQ ? NQ : 1];
   i32x4_t q4[QF == FMX ? NQ : 1];
@@ -513,6 +566,19 @@ void stage1_kernel(Stage1Args a) {
         qraw[4 * c + j] = u32x4_t{0u, 0u, 0u, 0u};
         if (d < kDqk) qraw[4 * c + j] = *reinterpret_cast<const u32x4_t*>(qrow + d);
       }
+  } else if constexpr (kQuantQ) {
+    // the fp8 B operand of chunk c holds dims 128c + 32g + [0, 32) in order
+    // (chunk 4: dims 512 + 32g + [0, 32) for g < 2, zeros otherwise); with
+    // four waves a wave loads only the chunks it quantises (c mod 4 = w)
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 128 * c + 32 * g + 8 * j;
+        qraw[4 * c + j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (d < kDqk && (kWaves != 4 || (c & 3) == w)) qraw[4 * c + j] = *reinterpret_cast<const u32x4_t*>(qrow + d);
+      }
   }
   // Over the bf16 cache, Q is loaded after the first tiles' DMAs are issued
   // (below): Q does not feed the gather chain (kv_indptr -> page ids ->
@@ -524,7 +590,7 @@ void stage1_kernel(Stage1Args a) {
   // kv_indptr -> page-id chain.
   constexpr bool kLateQ = KF == FBF16;
   auto load_q = [&]() {
-  if constexpr (kSplitQ) {
+  if constexpr (kSplitQ || kQuantQ) {
   } else if constexpr (QF == FBF16) {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
 #pragma unroll
@@ -568,7 +634,7 @@ void stage1_kernel(Stage1Args a) {
   }
   };
   if constexpr (!kLateQ) load_q();
-  if constexpr (QF == FFP8) qs = *static_cast<const float*>(a.q_scale);
+  if constexpr (QFE == FFP8) qs = *static_cast<const float*>(a.q_scale);
   if constexpr (KF == FFP8) ks = *static_cast<const float*>(a.kv_scale);
   float vs = 1.0f;  // split cache: V scale, applied with the final division
   if constexpr (KF == FMIX) vs = *a.kv2_scale;
@@ -774,9 +840,9 @@ void stage1_kernel(Stage1Args a) {
   // that Q as complete here, so its own wait for Q cannot drain the
   // in-flight tiles later.
   wait_vm<0>();
-  if constexpr (kSplitQ) {
-    // split after the first tile DMAs are issued (below): it then overlaps
-    // their latency instead of delaying them
+  if constexpr (kSplitQ || kQuantQ) {
+    // split or quantise after the first tile DMAs are issued (below): it
+    // then overlaps their latency instead of delaying them
 #pragma unroll
     for (int i = 0; i < 4 * NQ; ++i) asm volatile("" : "+v"(qraw[i]));
   } else if constexpr (!kLateQ) {
@@ -1109,11 +1175,50 @@ void stage1_kernel(Stage1Args a) {
     }
   };
 
+  // ---- bf16 Q quantised in the prologue: the first tile goes out, then Q
+  // is quantised while it and the next page ids are in flight (the fill
+  // below continues from the second tile).  Every wave takes part, streaming
+  // or not: with four waves each quantises only its share.
+  if constexpr (kQuantQ) {
+    if (nloc > 0) {
+      issue_pid(D);
+      issue_tile(0, 0, true);
+    }
+    const float r = 1.0f / qs;
+    const bool fast = qs >= 0x1p-60f && qs <= 0x1p60f;  // workgroup-uniform
+    auto quant = [&](int c) {
+      q8[c] = fast ? quant_q_fp8<false>(qraw + 4 * c, qs, r) : quant_q_fp8<true>(qraw + 4 * c, qs, r);
+    };
+    if constexpr (kWaves == 4) {
+      // chunk c is quantised by wave c mod 4 and shared through LDS
+      const int qx = static_cast<int>(smem0) + L::kTotal;
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+        if ((c & 3) == w) {
+          quant(c);
+          const u32x8_t u = __builtin_bit_cast(u32x8_t, q8[c]);
+          lds_st<u32x4_t>(qx + (c * 64 + lane) * 32, u32x4_t{u[0], u[1], u[2], u[3]});
+          lds_st<u32x4_t>(qx + (c * 64 + lane) * 32 + 16, u32x4_t{u[4], u[5], u[6], u[7]});
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+        const u32x4_t a0 = lds_ld<u32x4_t>(qx + (c * 64 + lane) * 32);
+        const u32x4_t a1 = lds_ld<u32x4_t>(qx + (c * 64 + lane) * 32 + 16);
+        q8[c] = __builtin_bit_cast(i32x8_t, u32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) quant(c);
+    }
+  }
+
   // ---- the asynchronous pipeline
   if (nloc > 0) {
     const int nfill = min(NBUF, nloc);
     int pend = -1;
-    for (int X = 0; X < nfill; ++X) {
+    for (int X = kQuantQ ? 1 : 0; X < nfill; ++X) {
       if (X >= D) wait_vm<D * NDMA + D - 1>();
       issue_pid(X + D);
       // split mode: the second fill tile leaves its rest to compute(0)
@@ -1559,7 +1664,9 @@ hipError_t launch_stage1_any(const Stage1Args& a, int32_t q_dtype, int32_t kv_dt
   const bool qb = q_dtype == MLA_DTYPE_BF16;
   if (kv_dtype == MLA_DTYPE_BF16) return launch_stage1<FBF16, FBF16>(a, grid, two_waves, st);
   if (kv_dtype == MLA_DTYPE_FP8_E4M3FN)
-    return qb ? launch_stage1<FBF16, FFP8>(a, grid, two_waves, st) : launch_stage1<FFP8, FFP8>(a, grid, two_waves, st);
+    return qb                                 ? launch_stage1<FBF16, FFP8>(a, grid, two_waves, st)
+           : q_dtype == MLA_Q_BF16_FP8_STATIC ? launch_stage1<FQ8S, FFP8>(a, grid, two_waves, st)
+                                              : launch_stage1<FFP8, FFP8>(a, grid, two_waves, st);
   if (kv_dtype == MLA_KV_MXFP4_K_FP8_V)
     return qb ? launch_stage1<FBF16, FMIX>(a, grid, two_waves, st) : launch_stage1<FMX, FMIX>(a, grid, two_waves, st);
   return qb ? launch_stage1<FBF16, FMX>(a, grid, two_waves, st) : launch_stage1<FMX, FMX>(a, grid, two_waves, st);

@@ -13,7 +13,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool supported_pair(int32_t qd, int32_t kd) {
   if (kd == MLA_DTYPE_BF16) return qd == MLA_DTYPE_BF16;
-  if (kd == MLA_DTYPE_FP8_E4M3FN) return qd == MLA_DTYPE_BF16 || qd == MLA_DTYPE_FP8_E4M3FN;
+  if (kd == MLA_DTYPE_FP8_E4M3FN)
+    return qd == MLA_DTYPE_BF16 || qd == MLA_DTYPE_FP8_E4M3FN || qd == MLA_Q_BF16_FP8_STATIC;
   if (kd == MLA_DTYPE_MXFP4) return qd == MLA_DTYPE_BF16 || qd == MLA_DTYPE_MXFP4;
   return false;
 }
@@ -53,7 +54,11 @@ const TuneEntry* tuned(int32_t batch, int32_t kv_len, int32_t q_dtype, int32_t k
   return nullptr;
 }
 
-int32_t valid_q(int32_t q) { return q == MLA_DTYPE_FP8_E4M3FN || q == MLA_DTYPE_MXFP4 ? q : MLA_DTYPE_BF16; }
+// bf16 Q quantised in the call runs the fp8-Q kernel: it takes fp8 Q's picks
+int32_t valid_q(int32_t q) {
+  if (q == MLA_Q_BF16_FP8_STATIC) return MLA_DTYPE_FP8_E4M3FN;
+  return q == MLA_DTYPE_FP8_E4M3FN || q == MLA_DTYPE_MXFP4 ? q : MLA_DTYPE_BF16;
+}
 int32_t valid_kv(int32_t kv) { return kv < MLA_DTYPE_BF16 || kv > MLA_KV_MXFP4_K_FP8_V ? MLA_DTYPE_FP8_E4M3FN : kv; }
 }  // namespace
 
@@ -112,7 +117,9 @@ int mla_validate(const void* q, int32_t q_dtype, const void* q_scale, const void
   if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out)) return MLA_ERR_ALIGN;
   if (kv_dtype == MLA_DTYPE_MXFP4 && !aligned16(kv_scale)) return MLA_ERR_ALIGN;
   if (kv_dtype == MLA_DTYPE_FP8_E4M3FN && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)) return MLA_ERR_ALIGN;
-  if (q_dtype == MLA_DTYPE_FP8_E4M3FN && (reinterpret_cast<uintptr_t>(q_scale) & 3u)) return MLA_ERR_ALIGN;
+  if ((q_dtype == MLA_DTYPE_FP8_E4M3FN || q_dtype == MLA_Q_BF16_FP8_STATIC) &&
+      (reinterpret_cast<uintptr_t>(q_scale) & 3u))
+    return MLA_ERR_ALIGN;
   const size_t need = mla_workspace_bytes(batch, num_splits);
   if (need) {
     if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;

@@ -8,6 +8,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import mla_latent_kv_13_amd as mla
 
@@ -38,7 +39,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
 
 
 def v(lib, q=A, qd=mla.BF16, qs=None, kv=A, kd=mla.BF16, ks=None, rows=100, ind=A, batch=4, pt=A,
@@ -55,6 +56,42 @@ def test_validate_ok_and_pairs(lib):
     for qd, kd in ((mla.FP8, mla.BF16), (mla.MXFP4, mla.BF16), (mla.FP8, mla.MXFP4), (mla.MXFP4, mla.FP8),
                    (mla.BF16, 7), (9, mla.BF16)):
         assert v(lib, qd=qd, qs=A2, kd=kd, ks=A2) == -2, (qd, kd)
+
+
+def test_validate_bf16_q_quantised_in_call(lib):
+    # bf16 Q quantised to fp8 inside the decode (static scale): fp8 cache only,
+    # the scale is required and must be 4-byte aligned
+    Q8 = mla.Q_BF16_FP8_STATIC
+    assert v(lib, qd=Q8, qs=A2, kd=mla.FP8, ks=A2) == 0
+    for kd in (mla.BF16, mla.MXFP4, mla.MIXED):
+        assert v(lib, qd=Q8, qs=A2, kd=kd, ks=A2) == -2, kd
+    assert v(lib, qd=Q8, qs=None, kd=mla.FP8, ks=A2) == -1
+    assert v(lib, qd=Q8, qs=A2 + 2, kd=mla.FP8, ks=A2) == -4
+    # it runs the fp8-Q kernel, so it takes fp8 Q's split counts and page sizes
+    for batch, L in ((4, 1024), (4, 8192), (32, 1024), (64, 8192), (256, 8192), (100, 3000)):
+        assert lib.mla_choose_num_splits(batch, L, Q8, mla.FP8, 256) == \
+            lib.mla_choose_num_splits(batch, L, mla.FP8, mla.FP8, 256)
+        assert lib.mla_recommend_page_size(batch, L, Q8, mla.FP8, 256) == \
+            lib.mla_recommend_page_size(batch, L, mla.FP8, mla.FP8, 256)
+
+
+def test_binding_q_fp8_scale_checks():
+    # argument checks of the binding's in-call fp8 Q mode (raised before any
+    # device work, so they run on CPU tensors)
+    kv8 = torch.zeros((64, 576), dtype=torch.float8_e4m3fn)
+    kvb = torch.zeros((64, 576), dtype=torch.bfloat16)
+    ind = torch.tensor([0, 8], dtype=torch.int32)
+    pt = torch.arange(8, dtype=torch.int32)
+    qb = torch.zeros((1, 16, 576), dtype=torch.bfloat16)
+    sc = torch.ones(1, dtype=torch.float32)
+    with pytest.raises(ValueError):  # bf16 cache
+        mla.decode(qb, kvb, ind, pt, 8, 1, q_fp8_scale=sc)
+    with pytest.raises(ValueError):  # fp8 Q given
+        mla.decode(qb.to(torch.float8_e4m3fn), kv8, ind, pt, 8, 1, kv_scale=sc, q_fp8_scale=sc)
+    with pytest.raises(ValueError):  # both scales
+        mla.decode(qb, kv8, ind, pt, 8, 1, q_scale=sc, kv_scale=sc, q_fp8_scale=sc)
+    with pytest.raises(ValueError):  # scale dtype
+        mla.decode(qb, kv8, ind, pt, 8, 1, kv_scale=sc, q_fp8_scale=sc.double())
 
 
 def test_validate_errors(lib):
