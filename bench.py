@@ -266,6 +266,14 @@ def time_workload(w, steps, warmup, device, warmup_s=0.3, extras=True):
                 mla.decode(r["q_bf16"], r["kv"], r["kv_indptr"], r["page_table"], w.page_size, S,
                            kv_scale=r["kv_scale"], out=r["out"], workspace=r["ws"], q_fp8_scale=r["q_scale_static"])
             res["us_q_quant_in_call"] = round(time_calls(call_qi, steps, warmup, 0.05, per_graph)[0] * 1e3, 3)
+        else:
+            # the same from bf16 Q with the mxfp4 quantiser inside the decode
+            # (MLA_Q_BF16_MXFP4)
+            def call_qi(i):
+                r = reps[i % nrep]
+                mla.decode(r["q_bf16"], r["kv"], r["kv_indptr"], r["page_table"], w.page_size, S,
+                           kv_scale=r["kv_scale"], out=r["out"], workspace=r["ws"], q_to_mxfp4=True)
+            res["us_q_quant_in_call"] = round(time_calls(call_qi, steps, warmup, 0.05, per_graph)[0] * 1e3, 3)
     if extras and nrep > 1:
         warm = time_calls(caller(S, 1), steps, warmup, 0.05, min(nrep, 64))[0]
         res["us_warm_same_buffers"] = round(warm * 1e3, 3)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3  /* 3: q_dtype MLA_Q_BF16_FP8_STATIC */
+#define MLA_ABI_VERSION 3  /* 3: q_dtypes MLA_Q_BF16_FP8_STATIC and MLA_Q_BF16_MXFP4 */
 
 /* Fixed MLA geometry (page 668813 module constants). */
 #define MLA_NUM_HEADS 16
@@ -71,6 +71,15 @@ extern "C" {
  * unspecified codes there and here). */
 #define MLA_Q_BF16_FP8_STATIC 4
 
+/* q_dtype only, with the mxfp4 cache: Q arrives as bf16 [batch,R,576] and the
+ * stage-1 workgroups quantise it to mxfp4 themselves (e2m1 codes with one
+ * e8m0 scale per 32 elements), code for code and scale for scale as
+ * mla_quantize_mxfp4, before decoding it as mxfp4 Q; q_scale is NULL.  Page
+ * 668813's mxfp4 route quantises Q to mxfp4 on every call.  The output is
+ * bit-identical to mla_quantize_mxfp4 followed by the decode with
+ * MLA_DTYPE_MXFP4 (NaN elements of Q give unspecified codes there and here). */
+#define MLA_Q_BF16_MXFP4 5
+
 /* Status codes. */
 #define MLA_OK 0
 #define MLA_ERR_NULL (-1)        /* a required pointer is NULL */
@@ -87,11 +96,12 @@ extern "C" {
 /*
  * mla_decode - split-K MLA decode of `batch` single-token requests.
  *
- * q          [batch,16,576] bf16            (q_dtype = MLA_DTYPE_BF16 or
- *                                            MLA_Q_BF16_FP8_STATIC), or
+ * q          [batch,16,576] bf16            (q_dtype = MLA_DTYPE_BF16,
+ *                                            MLA_Q_BF16_FP8_STATIC or
+ *                                            MLA_Q_BF16_MXFP4), or
  *            [batch,16,576] e4m3fn bytes    (q_dtype = MLA_DTYPE_FP8_E4M3FN), or
  *            [batch,16,288] packed e2m1     (q_dtype = MLA_DTYPE_MXFP4).
- * q_scale    NULL for bf16; device float[1] per-tensor scale for fp8 (the value
+ * q_scale    NULL for bf16 and MLA_Q_BF16_MXFP4; device float[1] per-tensor scale for fp8 (the value
  *            a code is multiplied by) and for MLA_Q_BF16_FP8_STATIC (the
  *            static scale Q is quantised with); device uint8 e8m0
  *            [batch*16, 18] for mxfp4.
@@ -119,8 +129,8 @@ extern "C" {
  *            bytes (may be NULL when that is 0); contents on entry are ignored.
  *
  * Supported (q, kv) pairs: (bf16,bf16), (bf16,fp8), (fp8,fp8), (bf16 quantised
- * to fp8 in the call, fp8), (bf16,mxfp4), (mxfp4,mxfp4); anything else
- * returns MLA_ERR_DTYPE.  q, kv_cache, out and
+ * to fp8 in the call, fp8), (bf16,mxfp4), (mxfp4,mxfp4), (bf16 quantised to
+ * mxfp4 in the call, mxfp4); anything else returns MLA_ERR_DTYPE.  q, kv_cache, out and
  * workspace must be 16-byte aligned.
  */
 int mla_decode(const void* q, int32_t q_dtype, const void* q_scale,

@@ -30,12 +30,13 @@ __all__ = [
     "load", "decode", "workspace_bytes", "choose_num_splits", "recommend_page_size",
     "quantize_fp8", "quantize_mxfp4", "validate", "status_string", "StatusError",
     "mxfp4_scale_buffer", "MIXED", "decode_mixed", "validate_mixed", "new_workspace", "decode_noalloc",
-    "NOALLOC_SCRATCH_BYTES", "Q_BF16_FP8_STATIC",
+    "NOALLOC_SCRATCH_BYTES", "Q_BF16_FP8_STATIC", "Q_BF16_MXFP4",
 ]
 
 BF16, FP8, MXFP4 = 0, 1, 2
 MIXED = 3  # split cache: mxfp4 K + fp8 V (format code for choose_num_splits)
 Q_BF16_FP8_STATIC = 4  # bf16 Q quantised to fp8 inside the decode with a static scale
+Q_BF16_MXFP4 = 5  # bf16 Q quantised to mxfp4 inside the decode
 HEADS, D_QK, D_V = 16, 576, 512
 MXFP4_ROW_BYTES, MXFP4_ROW_SCALES = 288, 18
 MAX_SPLITS = 256
@@ -213,7 +214,7 @@ def validate(q, kv_cache, kv_indptr, page_table, page_size, num_splits, *, q_sca
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Tensor,
            page_size: int, num_splits: int | None = None, *, q_scale=None, kv_scale=None,
            page_indptr=None, out=None, workspace=None, kv_len_hint: int | None = None, stream=None,
-           q_fp8_scale=None):
+           q_fp8_scale=None, q_to_mxfp4: bool = False):
     """MLA decode; returns out [batch,R,512] bf16 (enqueued on the current stream).
 
     q          [B,R,576] bf16 / float8_e4m3fn, or [B,R,288] uint8 (mxfp4, with q_scale e8m0 [B*R,18]);
@@ -223,6 +224,8 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
     q_fp8_scale  with bf16 q over the fp8 cache: a 1-element float32 static scale; the decode then
                quantises q to fp8 itself, code for code as quantize_fp8(q, q_fp8_scale)
                (MLA_Q_BF16_FP8_STATIC), in place of a separate quantiser launch
+    q_to_mxfp4 with bf16 q over the mxfp4 cache: the decode quantises q to mxfp4 itself, code for
+               code and scale for scale as quantize_mxfp4 (MLA_Q_BF16_MXFP4)
     """
     batch = kv_indptr.numel() - 1
     rows = _q_rows(q, batch)
@@ -234,6 +237,10 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, pag
         if q_fp8_scale.dtype != torch.float32 or q_fp8_scale.numel() < 1:
             raise ValueError("q_fp8_scale is a 1-element float32 tensor")
         q_scale, q_dtype = q_fp8_scale, Q_BF16_FP8_STATIC
+    if q_to_mxfp4:
+        if q.dtype != torch.bfloat16 or _fmt(kv_cache) != MXFP4 or q_scale is not None:
+            raise ValueError("q_to_mxfp4 takes bf16 q over the mxfp4 cache, without q_scale")
+        q_dtype = Q_BF16_MXFP4
     if num_splits is None:
         # one workgroup per 16-row query group: the occupancy is batch x groups
         hint = kv_len_hint if kv_len_hint is not None else max(1, kv_cache.shape[0] // max(batch, 1))

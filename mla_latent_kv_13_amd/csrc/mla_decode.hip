@@ -62,6 +62,7 @@ constexpr int FFP8 = MLA_DTYPE_FP8_E4M3FN;
 constexpr int FMX = MLA_DTYPE_MXFP4;
 constexpr int FMIX = MLA_KV_MXFP4_K_FP8_V;  // mxfp4 K + fp8 V, two caches
 constexpr int FQ8S = MLA_Q_BF16_FP8_STATIC;  // bf16 Q, quantised to fp8 in the prologue
+constexpr int FQ4 = MLA_Q_BF16_MXFP4;        // bf16 Q, quantised to mxfp4 in the prologue
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -455,12 +456,55 @@ __device__ __forceinline__ i32x8_t quant_q_fp8(const u32x4_t raw[4], float s, fl
   return __builtin_bit_cast(i32x8_t, out);
 }
 
+// The mxfp4 quantiser of bf16 Q on one lane's 32-element block (raw[0..3],
+// eight bf16 each, in element order): the rule of mla_quantize_mxfp4 (shared
+// exponent X = floor(log2 amax) - 2 clamped to [-127, 127], e8m0 = X + 127,
+// an all-zero block X = -127; code = nearest e2m1 value, ties to even,
+// saturating at 6, of v * 2^-X; element 2i in the low nibble of byte i).
+// v * 2^-X is ldexp(v, -X) exactly: for bf16 amax, X <= 125, so 2^-X is a
+// normal float and the product is exact or, when subnormal, rounded as
+// ldexp rounds.  On MI355X the hardware e2m1 encoder (scale 1) matched the
+// software encoder of mla_quantize_mxfp4 for every non-NaN fp32, and this
+// routine matched it on 2^20 random and special blocks.
+__device__ __forceinline__ void quant_q_mxfp4(const u32x4_t raw[4], i32x4_t& codes, uint32_t& e8) {
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * i + 2 * k] = __uint_as_float(raw[i][k] << 16);
+      v[8 * i + 2 * k + 1] = __uint_as_float(raw[i][k] & 0xffff0000u);
+    }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float a = __builtin_fabsf(v[i]);
+    amax = a > amax ? a : amax;  // NaN compares false and is skipped
+  }
+  int X = amax == 0.0f ? -127 : __builtin_amdgcn_frexp_expf(amax) - 3;
+  X = X < -127 ? -127 : (X > 126 ? 126 : X);
+  e8 = static_cast<uint32_t>(X + 127);
+  const float f = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
+  u32x4_t w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t d = 0;
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[8 * k + 0] * f, v[8 * k + 1] * f, 1.0f, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[8 * k + 2] * f, v[8 * k + 3] * f, 1.0f, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[8 * k + 4] * f, v[8 * k + 5] * f, 1.0f, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[8 * k + 6] * f, v[8 * k + 7] * f, 1.0f, 3);
+    w[k] = d;
+  }
+  codes = __builtin_bit_cast(i32x4_t, w);
+}
+
 template <int QF, int KF> struct QFrag;
 template <> struct QFrag<FBF16, FBF16> { static constexpr int kN = 18; };
 template <> struct QFrag<FBF16, FFP8> { static constexpr int kN = 18; };
 template <> struct QFrag<FBF16, FMX> { static constexpr int kN = 5; };  // hi/lo fp8 pairs
 template <> struct QFrag<FFP8, FFP8> { static constexpr int kN = 5; };
 template <> struct QFrag<FQ8S, FFP8> { static constexpr int kN = 5; };
+template <> struct QFrag<FQ4, FMX> { static constexpr int kN = 5; };
 template <> struct QFrag<FMX, FMX> { static constexpr int kN = 5; };
 template <> struct QFrag<FBF16, FMIX> { static constexpr int kN = 5; };
 template <> struct QFrag<FMX, FMIX> { static constexpr int kN = 5; };
@@ -486,11 +530,14 @@ void stage1_kernel(Stage1Args a) {
   constexpr int D = L::kD;
   constexpr int NDMA = L::kNdma;
   constexpr int ROW = Kv<KF>::kRow;
-  // bf16 Q quantised in the prologue by four-wave workgroups: each wave
-  // quantises some of the five fp8 B-operand chunks and they meet in LDS
-  // (10 KB past the rings; the 151 KB fp8 layout plus this still fits a CU)
-  constexpr int kQ8Bytes = QF == FQ8S && kWaves == 4 ? 5 * 64 * 32 : 0;
-  __shared__ __attribute__((aligned(1024))) char smem[L::kTotal + kQ8Bytes];
+  // bf16 Q quantised in the prologue: each wave quantises some of the five
+  // B-operand chunks and they meet in LDS past the rings - fp8 with four
+  // waves (10 KB; the 151 KB fp8 layout plus this still fits a CU), mxfp4
+  // with either wave count (6.25 KB of codes and scales)
+  constexpr bool kShareQ = (QF == FQ8S && kWaves == 4) || QF == FQ4;
+  constexpr int kQxBytes = !kShareQ ? 0 : QF == FQ8S ? 5 * 64 * 32 : 5 * 64 * 20;
+  __shared__ __attribute__((aligned(1024))) char smem[L::kTotal + kQxBytes];
+  static_assert((kWaves == 4 ? 1 : 2) * (L::kTotal + kQxBytes) <= 160 * 1024, "LDS of one CU exceeded");
   const uint32_t smem0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem));
 
   const int lane = threadIdx.x & 63;
@@ -544,14 +591,16 @@ void stage1_kernel(Stage1Args a) {
   // bf16 Q quantised here to fp8 with a static scale: raw bf16 fragments are
   // held until the loads have landed, then the rest is the fp8-Q kernel
   constexpr bool kQuantQ = QF == FQ8S;
-  constexpr int QFE = kQuantQ ? FFP8 : QF;  // the Q format the loop computes with
+  // bf16 Q quantised here to mxfp4 (per-block scales): likewise
+  constexpr bool kQuantQ4 = QF == FQ4;
+  constexpr int QFE = kQuantQ ? FFP8 : kQuantQ4 ? FMX : QF;  // the Q format the loop computes with
   bf16x8_t qb[QF == FBF16 && !kSplitQ ? NQ : 1];
-  u32x4_t qraw[kSplitQ || kQuantQ ? 4 * NQ : 1];
+  u32x4_t qraw[kSplitQ || kQuantQ || kQuantQ4 ? 4 * NQ : 1];
   i32x8_t q8[QFE == FFP8 || kSplitQ ? NQ : 1];
   i32x8_t ql[kSplitQ ? NQ : 1];
   uint32_t qhs[kSplitQ ? NQ : 1], qls[kSplitQ ? NQ : 1];
-  i32x4_t q4[QF == FMX ? NQ : 1];
-  uint32_t q4s[QF == FMX ? NQ : 1];
+  i32x4_t q4[QFE == FMX ? NQ : 1];
+  uint32_t q4s[QFE == FMX ? NQ : 1];
   float qs = 1.0f, ks = 1.0f;
   if constexpr (kSplitQ) {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
@@ -566,10 +615,11 @@ void stage1_kernel(Stage1Args a) {
         qraw[4 * c + j] = u32x4_t{0u, 0u, 0u, 0u};
         if (d < kDqk) qraw[4 * c + j] = *reinterpret_cast<const u32x4_t*>(qrow + d);
       }
-  } else if constexpr (kQuantQ) {
-    // the fp8 B operand of chunk c holds dims 128c + 32g + [0, 32) in order
-    // (chunk 4: dims 512 + 32g + [0, 32) for g < 2, zeros otherwise); with
-    // four waves a wave loads only the chunks it quantises (c mod 4 = w)
+  } else if constexpr (kQuantQ || kQuantQ4) {
+    // the fp8 B operand of chunk c holds dims 128c + 32g + [0, 32) in order,
+    // as does the mxfp4 one (one 32-element block per lane); chunk 4: dims
+    // 512 + 32g + [0, 32) for g < 2, zeros otherwise.  Where the waves share
+    // the work a wave loads only the chunks it quantises (c mod waves = w).
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
 #pragma unroll
     for (int c = 0; c < NQ; ++c)
@@ -577,7 +627,7 @@ void stage1_kernel(Stage1Args a) {
       for (int j = 0; j < 4; ++j) {
         const int d = 128 * c + 32 * g + 8 * j;
         qraw[4 * c + j] = u32x4_t{0u, 0u, 0u, 0u};
-        if (d < kDqk && (kWaves != 4 || (c & 3) == w)) qraw[4 * c + j] = *reinterpret_cast<const u32x4_t*>(qrow + d);
+        if (d < kDqk && (!kShareQ || c % kWaves == w)) qraw[4 * c + j] = *reinterpret_cast<const u32x4_t*>(qrow + d);
       }
   }
   // Over the bf16 cache, Q is loaded after the first tiles' DMAs are issued
@@ -590,7 +640,7 @@ void stage1_kernel(Stage1Args a) {
   // kv_indptr -> page-id chain.
   constexpr bool kLateQ = KF == FBF16;
   auto load_q = [&]() {
-  if constexpr (kSplitQ || kQuantQ) {
+  if constexpr (kSplitQ || kQuantQ || kQuantQ4) {
   } else if constexpr (QF == FBF16) {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(v) * kHeads + hq) * kDqk;
 #pragma unroll
@@ -840,7 +890,7 @@ void stage1_kernel(Stage1Args a) {
   // that Q as complete here, so its own wait for Q cannot drain the
   // in-flight tiles later.
   wait_vm<0>();
-  if constexpr (kSplitQ || kQuantQ) {
+  if constexpr (kSplitQ || kQuantQ || kQuantQ4) {
     // split or quantise after the first tile DMAs are issued (below): it
     // then overlaps their latency instead of delaying them
 #pragma unroll
@@ -1178,39 +1228,63 @@ void stage1_kernel(Stage1Args a) {
   // ---- bf16 Q quantised in the prologue: the first tile goes out, then Q
   // is quantised while it and the next page ids are in flight (the fill
   // below continues from the second tile).  Every wave takes part, streaming
-  // or not: with four waves each quantises only its share.
-  if constexpr (kQuantQ) {
+  // or not, since where the work is shared each wave quantises only its
+  // chunks (c mod waves = w) and reads the others' from LDS.
+  if constexpr (kQuantQ || kQuantQ4) {
     if (nloc > 0) {
       issue_pid(D);
       issue_tile(0, 0, true);
     }
-    const float r = 1.0f / qs;
-    const bool fast = qs >= 0x1p-60f && qs <= 0x1p60f;  // workgroup-uniform
-    auto quant = [&](int c) {
-      q8[c] = fast ? quant_q_fp8<false>(qraw + 4 * c, qs, r) : quant_q_fp8<true>(qraw + 4 * c, qs, r);
-    };
-    if constexpr (kWaves == 4) {
-      // chunk c is quantised by wave c mod 4 and shared through LDS
-      const int qx = static_cast<int>(smem0) + L::kTotal;
+    const int qx = static_cast<int>(smem0) + L::kTotal;
+    if constexpr (kQuantQ) {
+      const float r = 1.0f / qs;
+      const bool fast = qs >= 0x1p-60f && qs <= 0x1p60f;  // workgroup-uniform
+      auto quant = [&](int c) {
+        q8[c] = fast ? quant_q_fp8<false>(qraw + 4 * c, qs, r) : quant_q_fp8<true>(qraw + 4 * c, qs, r);
+      };
+      if constexpr (kShareQ) {
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+          if (c % kWaves == w) {
+            quant(c);
+            const u32x8_t u = __builtin_bit_cast(u32x8_t, q8[c]);
+            lds_st<u32x4_t>(qx + (c * 64 + lane) * 32, u32x4_t{u[0], u[1], u[2], u[3]});
+            lds_st<u32x4_t>(qx + (c * 64 + lane) * 32 + 16, u32x4_t{u[4], u[5], u[6], u[7]});
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+          const u32x4_t a0 = lds_ld<u32x4_t>(qx + (c * 64 + lane) * 32);
+          const u32x4_t a1 = lds_ld<u32x4_t>(qx + (c * 64 + lane) * 32 + 16);
+          q8[c] = __builtin_bit_cast(i32x8_t, u32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) quant(c);
+      }
+    } else {
+      // codes [c][lane] 16 B each, then scales [c][lane] 4 B each
+      const int qsx = qx + NQ * 64 * 16;
 #pragma unroll
       for (int c = 0; c < NQ; ++c) {
-        if ((c & 3) == w) {
-          quant(c);
-          const u32x8_t u = __builtin_bit_cast(u32x8_t, q8[c]);
-          lds_st<u32x4_t>(qx + (c * 64 + lane) * 32, u32x4_t{u[0], u[1], u[2], u[3]});
-          lds_st<u32x4_t>(qx + (c * 64 + lane) * 32 + 16, u32x4_t{u[4], u[5], u[6], u[7]});
+        if (c % kWaves == w) {
+          quant_q_mxfp4(qraw + 4 * c, q4[c], q4s[c]);
+          lds_st<i32x4_t>(qx + (c * 64 + lane) * 16, q4[c]);
+          lds_st<uint32_t>(qsx + (c * 64 + lane) * 4, q4s[c]);
         }
       }
       __syncthreads();
 #pragma unroll
       for (int c = 0; c < NQ; ++c) {
-        const u32x4_t a0 = lds_ld<u32x4_t>(qx + (c * 64 + lane) * 32);
-        const u32x4_t a1 = lds_ld<u32x4_t>(qx + (c * 64 + lane) * 32 + 16);
-        q8[c] = __builtin_bit_cast(i32x8_t, u32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+        q4[c] = lds_ld<i32x4_t>(qx + (c * 64 + lane) * 16);
+        q4s[c] = lds_ld<uint32_t>(qsx + (c * 64 + lane) * 4);
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) quant(c);
+      // dims 576..639 are padding, as in the mxfp4-Q load: zero codes, 2^0
+      if (g >= 2) {
+        q4[4] = i32x4_t{0, 0, 0, 0};
+        q4s[4] = 127u;
+      }
     }
   }
 
@@ -1218,7 +1292,7 @@ void stage1_kernel(Stage1Args a) {
   if (nloc > 0) {
     const int nfill = min(NBUF, nloc);
     int pend = -1;
-    for (int X = kQuantQ ? 1 : 0; X < nfill; ++X) {
+    for (int X = kQuantQ || kQuantQ4 ? 1 : 0; X < nfill; ++X) {
       if (X >= D) wait_vm<D * NDMA + D - 1>();
       issue_pid(X + D);
       // split mode: the second fill tile leaves its rest to compute(0)
@@ -1669,7 +1743,9 @@ hipError_t launch_stage1_any(const Stage1Args& a, int32_t q_dtype, int32_t kv_dt
                                               : launch_stage1<FFP8, FFP8>(a, grid, two_waves, st);
   if (kv_dtype == MLA_KV_MXFP4_K_FP8_V)
     return qb ? launch_stage1<FBF16, FMIX>(a, grid, two_waves, st) : launch_stage1<FMX, FMIX>(a, grid, two_waves, st);
-  return qb ? launch_stage1<FBF16, FMX>(a, grid, two_waves, st) : launch_stage1<FMX, FMX>(a, grid, two_waves, st);
+  return qb                            ? launch_stage1<FBF16, FMX>(a, grid, two_waves, st)
+         : q_dtype == MLA_Q_BF16_MXFP4 ? launch_stage1<FQ4, FMX>(a, grid, two_waves, st)
+                                       : launch_stage1<FMX, FMX>(a, grid, two_waves, st);
 }
 
 // Compute units of the current device (queried once per device; concurrent

@@ -15,7 +15,7 @@ bool supported_pair(int32_t qd, int32_t kd) {
   if (kd == MLA_DTYPE_BF16) return qd == MLA_DTYPE_BF16;
   if (kd == MLA_DTYPE_FP8_E4M3FN)
     return qd == MLA_DTYPE_BF16 || qd == MLA_DTYPE_FP8_E4M3FN || qd == MLA_Q_BF16_FP8_STATIC;
-  if (kd == MLA_DTYPE_MXFP4) return qd == MLA_DTYPE_BF16 || qd == MLA_DTYPE_MXFP4;
+  if (kd == MLA_DTYPE_MXFP4) return qd == MLA_DTYPE_BF16 || qd == MLA_DTYPE_MXFP4 || qd == MLA_Q_BF16_MXFP4;
   return false;
 }
 
@@ -54,9 +54,11 @@ const TuneEntry* tuned(int32_t batch, int32_t kv_len, int32_t q_dtype, int32_t k
   return nullptr;
 }
 
-// bf16 Q quantised in the call runs the fp8-Q kernel: it takes fp8 Q's picks
+// bf16 Q quantised in the call runs the fp8-Q or mxfp4-Q kernel: it takes
+// that format's picks
 int32_t valid_q(int32_t q) {
   if (q == MLA_Q_BF16_FP8_STATIC) return MLA_DTYPE_FP8_E4M3FN;
+  if (q == MLA_Q_BF16_MXFP4) return MLA_DTYPE_MXFP4;
   return q == MLA_DTYPE_FP8_E4M3FN || q == MLA_DTYPE_MXFP4 ? q : MLA_DTYPE_BF16;
 }
 int32_t valid_kv(int32_t kv) { return kv < MLA_DTYPE_BF16 || kv > MLA_KV_MXFP4_K_FP8_V ? MLA_DTYPE_FP8_E4M3FN : kv; }
@@ -111,7 +113,7 @@ int mla_validate(const void* q, int32_t q_dtype, const void* q_scale, const void
   if (!supported_pair(q_dtype, kv_dtype)) return MLA_ERR_DTYPE;
   if (batch == 0) return MLA_OK;  // nothing to do
   if (!q || !kv_cache || !kv_indptr || !page_table || !out) return MLA_ERR_NULL;
-  if (q_dtype != MLA_DTYPE_BF16 && !q_scale) return MLA_ERR_NULL;
+  if (q_dtype != MLA_DTYPE_BF16 && q_dtype != MLA_Q_BF16_MXFP4 && !q_scale) return MLA_ERR_NULL;
   if (kv_dtype != MLA_DTYPE_BF16 && !kv_scale) return MLA_ERR_NULL;
   if (num_kv_rows < 1) return MLA_ERR_ARG;
   if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out)) return MLA_ERR_ALIGN;
@@ -134,6 +136,8 @@ int mla_validate_mixed(const void* q, int32_t q_dtype, const void* q_scale, int3
                        const int32_t* page_indptr, int32_t page_size, int32_t num_splits, void* out,
                        void* workspace, size_t workspace_bytes) {
   if (q_rows < MLA_NUM_HEADS || q_rows % MLA_NUM_HEADS || q_rows > MLA_MAX_Q_ROWS) return MLA_ERR_ARG;
+  // Q is bf16 or mxfp4 (no in-call quantisation over the split cache)
+  if (q_dtype != MLA_DTYPE_BF16 && q_dtype != MLA_DTYPE_MXFP4) return MLA_ERR_DTYPE;
   // the K side is an mxfp4 cache in every respect; its workspace check is
   // for 16 rows, so it is redone below for q_rows
   int rc = mla_validate(q, q_dtype, q_scale, k_cache, MLA_DTYPE_MXFP4, k_scale, num_kv_rows, kv_indptr, batch,

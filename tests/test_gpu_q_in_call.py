@@ -1,14 +1,15 @@
-"""GPU: bf16 Q quantised to fp8 inside the decode (q_dtype MLA_Q_BF16_FP8_STATIC).
+"""GPU: bf16 Q quantised inside the decode (q_dtype MLA_Q_BF16_FP8_STATIC over
+the fp8 cache, MLA_Q_BF16_MXFP4 over the mxfp4 cache).
 
-The stage-1 workgroups quantise bf16 Q themselves with a static per-tensor
-scale, code for code as mla_quantize_fp8 does.  So the decode's output must
-equal, bit for bit, the output of mla_quantize_fp8 followed by the fp8-Q
-decode on the same scale: any code that differed would change its logits.
-The Q tensors hold every finite bf16 bit pattern (zeros of both signs,
-subnormals, values far beyond the +-448 clamp, infinities), and the scales
-include ones outside the reciprocal-division range, which take the plain
-division.  The oracle check runs the fused path against the fp64 oracle on
-the oracle's own fp8 codes of Q, like the other parity tests.
+The stage-1 workgroups quantise bf16 Q themselves, code for code as
+mla_quantize_fp8 (static scale) or mla_quantize_mxfp4 does.  So the decode's
+output must equal, bit for bit, the output of that quantiser followed by the
+fp8-Q or mxfp4-Q decode: any code or block scale that differed would change
+its logits.  The Q tensors hold every non-NaN bf16 bit pattern (zeros of both
+signs, subnormals, values far beyond the fp8 clamp, infinities); the fp8
+scales include ones outside the reciprocal-division range, which take the
+plain division.  The oracle checks run the in-call paths against the fp64
+oracle on the oracle's own codes of Q, like the other parity tests.
 """
 import numpy as np
 import pytest
@@ -40,6 +41,21 @@ def all_finite_bf16(shape, seed):
 def fp8_cache(case):
     kv, ks = mla.quantize_fp8(case["kv"].to(DEV))
     return kv, ks, case["kv_indptr"].to(DEV), case["page_table"].to(DEV)
+
+
+def mxfp4_cache(case):
+    kv, ks = mla.quantize_mxfp4(case["kv"].to(DEV))
+    return kv, ks, case["kv_indptr"].to(DEV), case["page_table"].to(DEV)
+
+
+def both_paths_mx(q, kv, ks, ind, pt, P, S):
+    """(in-call mxfp4 quantisation, separate quantiser + mxfp4-Q decode) outputs."""
+    B, R = q.shape[0], q.shape[1]
+    q4, s4 = mla.quantize_mxfp4(q.reshape(B * R, 576))
+    fused = mla.decode(q, kv, ind, pt, P, S, kv_scale=ks, q_to_mxfp4=True)
+    two = mla.decode(q4.reshape(B, R, 288), kv, ind, pt, P, S, q_scale=s4, kv_scale=ks)
+    torch.cuda.synchronize()
+    return fused, two
 
 
 def both_paths(q, kv, ks, ind, pt, P, S, scale):
@@ -109,3 +125,56 @@ def test_in_call_q8_full_size(name):
     kv, ks, ind, pt = fp8_cache(case)
     fused, two = both_paths(case["q"].to(DEV), kv, ks, ind, pt, w.page_size, S, w.q_scale)
     assert_same_bits(fused, two, name)
+
+
+# ----------------------------------------------------------- mxfp4 Q
+@pytest.mark.parametrize("S", [1, 2])
+def test_in_call_mxfp4_every_bf16_pattern(S):
+    lengths = [100, 37, 300, 1, 64, 129, 0, 250]
+    print(f"[q4-in-call] every bf16 pattern, S={S}", flush=True)
+    case = synth.make_case(len(lengths), lengths, 8, shuffle=True, seed=920 + S)
+    q = all_finite_bf16((len(lengths), 16, 576), seed=921).to(DEV)
+    kv, ks, ind, pt = mxfp4_cache(case)
+    fused, two = both_paths_mx(q, kv, ks, ind, pt, 8, S)
+    assert_same_bits(fused, two, f"mxfp4 S {S}")
+    assert not fused[6].any()
+
+
+@pytest.mark.parametrize("batch,length,rows,S", [
+    (300, 40, 16, 1),    # 300 workgroups: the two-wave layout
+    (300, 40, 16, 2),
+    (8, 700, 64, 2),     # four query groups per request
+    (3, 2048, 16, 32),
+])
+def test_in_call_mxfp4_layouts(batch, length, rows, S):
+    print(f"[q4-in-call] batch={batch} L={length} rows={rows} S={S}", flush=True)
+    case = synth.make_case(batch, length, 8, shuffle=True, seed=930 + S)
+    q = synth.normal_bf16((batch, rows, 576), seed=931, device=DEV, std=2.0)
+    kv, ks, ind, pt = mxfp4_cache(case)
+    fused, two = both_paths_mx(q, kv, ks, ind, pt, 8, S)
+    assert_same_bits(fused, two, f"mxfp4 batch {batch} rows {rows} S {S}")
+
+
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+def test_in_call_mxfp4_matches_oracle(orc, shape):
+    lengths, P, S, per_req = SHAPES[shape]
+    print(f"[q4-in-call] oracle lengths={lengths} P={P} S={S} per_request={per_req}", flush=True)
+    case = synth.make_case(len(lengths), lengths, P, shuffle=True, seed=400 + shape, per_request_pages=per_req,
+                           extra_pages=2)
+    g, o = prepare(case, "mxfp4", "mxfp4", orc)  # asserts the quantisers' codes agree
+    out = mla.decode(case["q"].to(DEV), g["kv"], g["kv_indptr"], g["page_table"], case["page_size"], S,
+                     kv_scale=g["kv_scale"], page_indptr=g["page_indptr"], q_to_mxfp4=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle_decode(case, o, orc)
+    check_close(out, ref, what=f"in-call mxfp4 Q, shape {shape}")
+    assert_same_bits(out, gpu_decode(case, g, S), f"mxfp4 shape {shape}")
+
+
+@pytest.mark.parametrize("S", [2, 1])
+def test_in_call_mxfp4_full_size(S):
+    w = synth.WORKLOADS["bs256_kv8192_mxfp4_q4"]
+    print(f"[q4-in-call] full size {w.name} S={S}", flush=True)
+    case = synth.workload_case(w)
+    kv, ks, ind, pt = mxfp4_cache(case)
+    fused, two = both_paths_mx(case["q"].to(DEV), kv, ks, ind, pt, w.page_size, S)
+    assert_same_bits(fused, two, f"{w.name} S {S}")

@@ -75,6 +75,20 @@ def test_validate_bf16_q_quantised_in_call(lib):
             lib.mla_recommend_page_size(batch, L, mla.FP8, mla.FP8, 256)
 
 
+def test_validate_bf16_q_quantised_to_mxfp4_in_call(lib):
+    # bf16 Q quantised to mxfp4 inside the decode: mxfp4 cache only, no Q scale
+    Q4 = mla.Q_BF16_MXFP4
+    assert v(lib, qd=Q4, qs=None, kd=mla.MXFP4, ks=A2) == 0
+    for kd in (mla.BF16, mla.FP8, mla.MIXED):
+        assert v(lib, qd=Q4, qs=None, kd=kd, ks=A2) == -2, kd
+    for batch, L in ((4, 1024), (32, 8192), (256, 8192), (100, 3000)):
+        assert lib.mla_choose_num_splits(batch, L, Q4, mla.MXFP4, 256) == \
+            lib.mla_choose_num_splits(batch, L, mla.MXFP4, mla.MXFP4, 256)
+    # not over the split cache (mxfp4 K + fp8 V)
+    rc = lib.mla_validate_mixed(A, Q4, None, 16, A, A2, A, A2, 100, A, 4, A, None, 1, 1, A, None, 0)
+    assert rc == -2
+
+
 def test_binding_q_fp8_scale_checks():
     # argument checks of the binding's in-call fp8 Q mode (raised before any
     # device work, so they run on CPU tensors)
@@ -92,6 +106,8 @@ def test_binding_q_fp8_scale_checks():
         mla.decode(qb, kv8, ind, pt, 8, 1, q_scale=sc, kv_scale=sc, q_fp8_scale=sc)
     with pytest.raises(ValueError):  # scale dtype
         mla.decode(qb, kv8, ind, pt, 8, 1, kv_scale=sc, q_fp8_scale=sc.double())
+    with pytest.raises(ValueError):  # mxfp4 quantisation needs the mxfp4 cache
+        mla.decode(qb, kv8, ind, pt, 8, 1, kv_scale=sc, q_to_mxfp4=True)
 
 
 def test_validate_errors(lib):
