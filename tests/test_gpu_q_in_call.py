@@ -18,7 +18,7 @@ import torch
 import mla_latent_kv_13_amd as mla
 from mla_latent_kv_13_amd import synth
 
-from test_gpu_parity import DEV, SHAPES, bits, check_close, gpu_decode, oracle_decode, prepare
+from test_gpu_parity import DEV, RANDOM_SCALE, SHAPES, bits, check_close, gpu_decode, oracle_decode, prepare
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +178,38 @@ def test_in_call_mxfp4_full_size(S):
     kv, ks, ind, pt = mxfp4_cache(case)
     fused, two = both_paths_mx(case["q"].to(DEV), kv, ks, ind, pt, w.page_size, S)
     assert_same_bits(fused, two, f"{w.name} S {S}")
+
+
+# ------------------------------------------------------ random layouts
+@pytest.mark.parametrize("i", range(16 * RANDOM_SCALE))
+def test_in_call_random_configurations(i):
+    """Seeded random layouts (ragged lengths with empty and one-token
+    requests, any page size, both paging conventions, 16-128 query rows,
+    S up to 64) for both in-call modes, bit for bit against the separate
+    quantiser followed by the decode."""
+    rng = np.random.default_rng(11000 + i)
+    batch = int(rng.integers(1, 7))
+    lengths = [0 if u < 0.12 else 1 if u < 0.24 else int(rng.integers(2, 2500)) for u in rng.random(batch)]
+    P = int(rng.choice([1, 2, 3, 5, 8, 16, 32]))
+    per_req = bool(rng.random() < 0.5)
+    S = int(rng.choice([1, 2, 3, 4, 5, 8, 13, 16, 32, 64]))
+    rows = int(rng.choice([16, 16, 32, 64, 128]))
+    mode = "fp8" if i % 2 == 0 else "mxfp4"
+    print(f"[in-call random {i}] {mode} rows={rows} lengths={lengths} P={P} S={S} per_request={per_req}",
+          flush=True)
+    case = synth.make_case(batch, lengths, P, shuffle=True, seed=11100 + i, per_request_pages=per_req,
+                           extra_pages=1)
+    q = synth.normal_bf16((batch, rows, 576), seed=11200 + i, device=DEV, std=float(rng.choice([0.1, 1.0, 30.0])))
+    pind = None if case["page_indptr"] is None else case["page_indptr"].to(DEV)
+    if mode == "fp8":
+        kv, ks, ind, pt = fp8_cache(case)
+        q8, sc = mla.quantize_fp8(q, 6.0 / 448.0)
+        fused = mla.decode(q, kv, ind, pt, P, S, kv_scale=ks, q_fp8_scale=sc, page_indptr=pind)
+        two = mla.decode(q8, kv, ind, pt, P, S, q_scale=sc, kv_scale=ks, page_indptr=pind)
+    else:
+        kv, ks, ind, pt = mxfp4_cache(case)
+        q4, s4 = mla.quantize_mxfp4(q.reshape(batch * rows, 576))
+        fused = mla.decode(q, kv, ind, pt, P, S, kv_scale=ks, q_to_mxfp4=True, page_indptr=pind)
+        two = mla.decode(q4.reshape(batch, rows, 288), kv, ind, pt, P, S, q_scale=s4, kv_scale=ks, page_indptr=pind)
+    torch.cuda.synchronize()
+    assert_same_bits(fused, two, f"in-call random {i}")
