@@ -234,7 +234,9 @@ int32_t mla_recommend_page_size(int32_t batch, int32_t kv_len, int32_t q_dtype, 
  * mla_decode_rows - mla_decode for q_rows query rows per request: q_seq_len
  * query tokens x num_heads heads (multi-token decode, or more than 16 heads),
  * flattened row-major into q [batch, q_rows, 576] (mxfp4: [batch, q_rows,
- * 288] with e8m0 q_scale [batch*q_rows, 18]); out is [batch, q_rows, 512].
+ * 288] with e8m0 q_scale [batch*q_rows, 18]; the in-call quantisation modes
+ * MLA_Q_BF16_FP8_STATIC and MLA_Q_BF16_MXFP4 take bf16 rows as mla_decode
+ * does); out is [batch, q_rows, 512].
  * Every row attends to its request's whole cache with no mask, as page
  * 695854's chunked torch fallback treats q_seq_len x num_heads rows (its
  * aiter route takes q_seq_len 4 with 16, 32 or 64 heads).  q_rows is a
